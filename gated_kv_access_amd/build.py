@@ -1,0 +1,48 @@
+"""Builds liboda.so, the C-ABI library of the ODA decode path, for gfx950.
+
+oda_api.cpp (validation, planning, launch order) is plain host C++ and is
+compiled with g++; oda_kernels.hip is compiled with hipcc for gfx950; the two
+objects are linked by hipcc into gated_kv_access_amd/liboda.so.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "liboda.so")
+BUILD = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed-fp32 VALU forms are kept out of every HIP object.
+HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, extra_hip_flags=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    api_o = os.path.join(BUILD, "oda_api.o")
+    ker_o = os.path.join(BUILD, "oda_kernels.o")
+    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "oda_api.cpp"), "-o", api_o], verbose)
+    _run([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-c", os.path.join(CSRC, "oda_kernels.hip"), "-o", ker_o],
+         verbose)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

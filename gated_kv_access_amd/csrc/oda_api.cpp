@@ -1,0 +1,414 @@
+// oda_api.cpp -- the extern "C" entry points declared in include/oda.h:
+// argument validation, planning (split counts, workspace carve-up) and the
+// order of launches of one decode step.  Validation runs before any HIP call,
+// so argument errors are reported on a machine without a GPU.
+//
+// Step order follows the picx.dev summary of "On-Demand Attention", section
+// "Local-First Decoding": Local pass of every layer, then the recall-score
+// gate, then (for requests whose score exceeds theta) the Full recomputation
+// of every layer; section "Efficient Execution": one fused commit of the new
+// token's K/V for all layers.
+#include <math.h>
+#include <string.h>
+
+#include "oda_internal.h"
+
+using oda::Plan;
+using oda::WsLayout;
+
+namespace {
+
+constexpr int32_t kDefaultFullGroups = 1024;  // workgroups a Full pass aims for
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Validates dims and derives the plan; ODA_OK or the error to return.
+oda_status make_plan(const oda_dims* d, Plan* p) {
+  if (!d || !p) return ODA_ERR_INVALID_ARG;
+  memset(p, 0, sizeof *p);
+  if (d->num_layers < 1 || d->num_layers > ODA_MAX_LAYERS) return ODA_ERR_INVALID_ARG;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1) return ODA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return ODA_ERR_INVALID_ARG;
+  if (d->head_dim < 1 || d->kv_dtype < 0 || d->kv_dtype > 1) return ODA_ERR_INVALID_ARG;
+  if (d->sink < 0 || d->max_batch < 1 || d->max_batch > ODA_MAX_BATCH) return ODA_ERR_INVALID_ARG;
+  if (d->full_splits < 0 || d->local_splits < 0 || d->reserved0 != 0) return ODA_ERR_INVALID_ARG;
+  if (!(d->softmax_scale >= 0.f) || isinf(d->softmax_scale)) return ODA_ERR_INVALID_ARG;
+  if (d->recall_flops < 0 || (d->focus != 0 && d->focus != 1)) return ODA_ERR_INVALID_ARG;
+  p->L = d->num_layers;
+  p->Hq = d->num_q_heads;
+  p->Hkv = d->num_kv_heads;
+  p->D = d->head_dim;
+  p->G = d->num_q_heads / d->num_kv_heads;
+  p->dtype = d->kv_dtype;
+  p->esize = d->kv_dtype == ODA_BF16 ? 2 : 4;
+  p->sink = d->sink;
+  p->window = d->window;
+  p->sw_window = d->sw_window;
+  p->focus = d->focus;
+  p->max_batch = d->max_batch;
+  p->max_blocks = d->max_blocks_per_seq;
+  p->block_size = d->block_size;
+  p->recall_flops = d->recall_flops;
+  int16_t ng = 0, ns = 0;
+  for (int l = 0; l < p->L; ++l) {
+    const uint8_t k = d->layer_kind ? d->layer_kind[l] : (uint8_t)ODA_LAYER_GATED;
+    if (k != ODA_LAYER_GATED && k != ODA_LAYER_SLIDING) return ODA_ERR_INVALID_ARG;
+    p->kind[l] = k;
+    p->kidx[l] = k == ODA_LAYER_GATED ? ng++ : ns++;
+  }
+  p->Lg = ng;
+  p->Ls = ns;
+  if (p->Lg > 0) {
+    if (d->window < 1 || !is_pow2(d->block_size) || d->max_blocks_per_seq < 1) return ODA_ERR_INVALID_ARG;
+    if ((int64_t)d->max_blocks_per_seq * d->block_size > (int64_t)1 << 30) return ODA_ERR_INVALID_ARG;
+    if ((int64_t)d->sink + d->window > (int64_t)1 << 24) return ODA_ERR_INVALID_ARG;
+  }
+  if (p->Ls > 0 && (d->sw_window < 1 || d->sw_window > (1 << 24))) return ODA_ERR_INVALID_ARG;
+  // Built variants: d in {64, 128}, group in {1, 2, 4}.
+  if (p->D != 64 && p->D != 128) return ODA_ERR_UNSUPPORTED;
+  if (p->G != 1 && p->G != 2 && p->G != 4) return ODA_ERR_UNSUPPORTED;
+  p->ring_slots = p->Lg > 0 ? p->sink + p->window : 0;
+  p->block_shift = 0;
+  if (p->Lg > 0)
+    while ((1 << p->block_shift) < p->block_size) ++p->block_shift;
+  const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)p->D);
+  p->scale_log2 = scale * 1.44269504088896340736f;
+  p->tile_rows = oda::tile_rows_for(p->dtype, p->D);
+  return ODA_OK;
+}
+
+// Split counts depend only on dims and batch, so the workspace size does too.
+void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
+  const int32_t tile = p->tile_rows;
+  const int32_t b = batch > 0 ? batch : 1;
+  if (p->Lg > 0) {
+    const int64_t max_ctx = (int64_t)p->max_blocks * p->block_size;
+    const int32_t tiles = ceil_div(max_ctx, tile);
+    int32_t f = d->full_splits > 0 ? d->full_splits : ceil_div(kDefaultFullGroups, (int64_t)b * p->Hkv);
+    if (f > tiles) f = tiles;
+    p->full_splits = f < 1 ? 1 : f;
+    const int32_t rtiles = ceil_div(p->ring_slots, tile);
+    int32_t l = d->local_splits > 0 ? d->local_splits : rtiles;
+    if (l > rtiles) l = rtiles;
+    p->local_splits = l < 1 ? 1 : l;
+  }
+  if (p->Ls > 0) {
+    const int32_t stiles = ceil_div(p->sw_window, tile);
+    int32_t s = d->local_splits > 0 ? d->local_splits : stiles;
+    if (s > stiles) s = stiles;
+    p->sw_splits = s < 1 ? 1 : s;
+  }
+}
+
+WsLayout layout(const Plan& p, int32_t batch) {
+  WsLayout w{};
+  const int32_t b = batch > 0 ? batch : 1;
+  int32_t ms = p.full_splits;
+  if (p.local_splits > ms) ms = p.local_splits;
+  if (p.sw_splits > ms) ms = p.sw_splits;
+  w.max_splits = ms;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.err_off = 0;
+  w.count_off = 4;
+  w.list_off = oda::kWsHeader;
+  w.part_o_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
+  w.total = up(w.part_ml_off + sizeof(float) * 2 * (size_t)b * p.Hq * ms);
+  return w;
+}
+
+struct Ctx {
+  Plan plan;
+  WsLayout ws;
+  char* base;
+  uint32_t* err;
+};
+
+oda_status prepare(const oda_dims* dims, int32_t batch, void* workspace, size_t ws_bytes, Ctx* c,
+                   bool need_ws = true) {
+  oda_status st = make_plan(dims, &c->plan);
+  if (st != ODA_OK) return st;
+  if (batch < 0 || batch > c->plan.max_batch) return ODA_ERR_INVALID_ARG;
+  choose_splits(dims, batch, &c->plan);
+  c->ws = layout(c->plan, batch);
+  if (need_ws) {
+    if (!workspace || ws_bytes < c->ws.total) return ODA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return ODA_ERR_WORKSPACE;
+  }
+  c->base = static_cast<char*>(workspace);
+  c->err = workspace ? reinterpret_cast<uint32_t*>(c->base + c->ws.err_off) : nullptr;
+  return ODA_OK;
+}
+
+bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
+
+oda_status check_kv(const Plan& p, const oda_kv* kv, bool need_gated_cache, bool need_rings) {
+  if (!kv || !kv->seq_len) return ODA_ERR_INVALID_ARG;
+  if (need_gated_cache && p.Lg > 0) {
+    if (!kv->k_cache || !kv->v_cache || !kv->block_table || kv->num_blocks < 1) return ODA_ERR_INVALID_ARG;
+    if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache)) return ODA_ERR_INVALID_ARG;
+  }
+  if (need_rings) {
+    if (p.Lg > 0 && (!kv->k_ring || !kv->v_ring || !kv->ring_pos)) return ODA_ERR_INVALID_ARG;
+    if (p.Ls > 0 && (!kv->k_swring || !kv->v_swring || !kv->swring_pos)) return ODA_ERR_INVALID_ARG;
+    if (p.Lg > 0 && (!aligned16(kv->k_ring) || !aligned16(kv->v_ring))) return ODA_ERR_INVALID_ARG;
+    if (p.Ls > 0 && (!aligned16(kv->k_swring) || !aligned16(kv->v_swring))) return ODA_ERR_INVALID_ARG;
+  }
+  if (p.focus && p.Lg > 0 && !kv->focus_range) return ODA_ERR_INVALID_ARG;
+  return ODA_OK;
+}
+
+oda_status hip_status(int rc) { return rc == 0 ? ODA_OK : ODA_ERR_HIP; }
+
+// Attention pass of one layer: `full` selects the gated Full pass.
+oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, bool full,
+                    const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
+                    const int32_t* call_list, const int32_t* call_count, oda_stream s) {
+  const Plan& p = c.plan;
+  const bool gated = p.kind[layer] == ODA_LAYER_GATED;
+  oda::AttnParams a{};
+  a.rows.source = (gated && full) ? oda::kSrcPaged : oda::kSrcRing;
+  a.rows.focus = p.focus;
+  a.rows.sink = gated ? p.sink : 0;
+  a.rows.window = gated ? p.window : p.sw_window;
+  a.rows.ring_slots = gated ? p.ring_slots : p.sw_window;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.splits = a.rows.source == oda::kSrcPaged ? p.full_splits : (gated ? p.local_splits : p.sw_splits);
+  a.tile_rows = p.tile_rows;
+  a.max_blocks = p.max_blocks;
+  a.block_shift = p.block_shift;
+  a.num_blocks = kv->num_blocks;
+  const int64_t row_bytes = (int64_t)p.D * p.esize;
+  const int64_t rank = p.kidx[layer];
+  if (a.rows.source == oda::kSrcPaged) {
+    const int64_t layer_bytes = kv->num_blocks * p.Hkv * p.block_size * row_bytes;
+    a.k_base = static_cast<const char*>(kv->k_cache) + rank * layer_bytes;
+    a.v_base = static_cast<const char*>(kv->v_cache) + rank * layer_bytes;
+  } else {
+    const int64_t layer_bytes = (int64_t)p.max_batch * p.Hkv * a.rows.ring_slots * row_bytes;
+    a.k_base = static_cast<const char*>(gated ? kv->k_ring : kv->k_swring) + rank * layer_bytes;
+    a.v_base = static_cast<const char*>(gated ? kv->v_ring : kv->v_swring) + rank * layer_bytes;
+  }
+  a.block_table = kv->block_table;
+  a.seq_len = kv->seq_len;
+  a.focus_range = kv->focus_range;
+  a.call_list = full ? call_list : nullptr;
+  a.call_count = full ? call_count : nullptr;
+  a.q = q;
+  a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
+  a.err = c.err;
+  a.scale_log2 = p.scale_log2;
+  a.capacity = p.max_blocks * p.block_size;
+  int rc = oda::launch_attention(p, a, batch, s);
+  if (rc) return ODA_ERR_HIP;
+  oda::MergeParams m{};
+  m.rows = a.rows;
+  m.Hq = p.Hq;
+  m.Hkv = p.Hkv;
+  m.splits = a.splits;
+  m.tile_rows = p.tile_rows;
+  m.capacity = a.capacity;
+  m.seq_len = kv->seq_len;
+  m.focus_range = kv->focus_range;
+  m.call_list = a.call_list;
+  m.call_count = a.call_count;
+  m.q = q;
+  m.k_cur = k_cur;
+  m.v_cur = v_cur;
+  m.part_o = a.part_o;
+  m.part_ml = a.part_ml;
+  m.out = out;
+  m.lse = lse;
+  m.scale_log2 = p.scale_log2;
+  return hip_status(oda::launch_merge(p, m, batch, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t oda_workspace_size(const oda_dims* dims, int32_t batch) {
+  Ctx c;
+  if (prepare(dims, batch, nullptr, 0, &c, false) != ODA_OK) return 0;
+  return c.ws.total;
+}
+
+oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspace, size_t bytes,
+                              oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, bytes, &c);
+  if (st != ODA_OK) return st;
+  return hip_status(oda::launch_clear(workspace, c.ws.total, stream));
+}
+
+oda_status oda_prefill_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch, int32_t layer,
+                          const void* k_src, const void* v_src, int64_t src_rows, void* workspace,
+                          size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (layer < 0 || layer >= c.plan.L || !k_src || !v_src || src_rows < 0) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src)) return ODA_ERR_INVALID_ARG;
+  const bool gated = c.plan.kind[layer] == ODA_LAYER_GATED;
+  st = check_kv(c.plan, kv, gated, true);
+  if (st != ODA_OK) return st;
+  return hip_status(oda::launch_prefill(c.plan, *kv, batch, layer, k_src, v_src, src_rows, c.err, stream));
+}
+
+oda_status oda_ring_init(const oda_dims* dims, const oda_kv* kv, int32_t batch, void* workspace,
+                         size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  st = check_kv(c.plan, kv, true, true);
+  if (st != ODA_OK) return st;
+  return hip_status(oda::launch_ring_init(c.plan, *kv, batch, c.err, stream));
+}
+
+oda_status oda_commit_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch, const void* k_new,
+                         const void* v_new, void* workspace, size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return ODA_ERR_INVALID_ARG;
+  st = check_kv(c.plan, kv, true, true);
+  if (st != ODA_OK) return st;
+  return hip_status(oda::launch_commit(c.plan, *kv, batch, k_new, v_new, c.err, stream));
+}
+
+oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
+                            const void* q, const void* k_cur, const void* v_cur, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (layer < 0 || layer >= c.plan.L || !q || !k_cur || !v_cur || !out) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q)) return ODA_ERR_INVALID_ARG;
+  st = check_kv(c.plan, kv, false, true);
+  if (st != ODA_OK) return st;
+  return run_pass(c, kv, layer, batch, false, q, k_cur, v_cur, out, lse, nullptr, nullptr, stream);
+}
+
+oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
+                                 const void* q, const void* k_cur, const void* v_cur,
+                                 const float* recall_score, float theta, float* out, float* lse,
+                                 int32_t* call_list, int32_t* call_count, void* workspace,
+                                 size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (layer < 0 || layer >= c.plan.L || !q || !k_cur || !v_cur || !out || !recall_score)
+    return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q) || isnan(theta)) return ODA_ERR_INVALID_ARG;
+  const bool gated = c.plan.kind[layer] == ODA_LAYER_GATED;
+  st = check_kv(c.plan, kv, gated, !gated);
+  if (st != ODA_OK) return st;
+  int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
+  int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
+  int rc = oda::launch_gate(c.plan, *kv, batch, recall_score, theta, list, count, nullptr, nullptr, stream);
+  if (rc) return ODA_ERR_HIP;
+  return run_pass(c, kv, layer, batch, true, q, k_cur, v_cur, out, lse, list, count, stream);
+}
+
+oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch, const float* recall_score,
+                    float theta, int32_t* call_list, int32_t* call_count, int64_t* full_calls,
+                    int64_t* counters, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, nullptr, 0, &c, false);
+  if (st != ODA_OK) return st;
+  if (!recall_score || isnan(theta) || !kv || !kv->seq_len) return ODA_ERR_INVALID_ARG;
+  if (c.plan.focus && c.plan.Lg > 0 && counters && !kv->focus_range) return ODA_ERR_INVALID_ARG;
+  return hip_status(oda::launch_gate(c.plan, *kv, batch, recall_score, theta, call_list, call_count,
+                                     full_calls, counters, stream));
+}
+
+oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const void* q_local,
+                    const void* q_full, const void* k_new, const void* v_new,
+                    const float* recall_score, float theta, float* out, float* lse,
+                    int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                    void* workspace, size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (!q_local || !k_new || !v_new || !recall_score || !out || isnan(theta)) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q_local) || (q_full && !aligned16(q_full)) || !aligned16(k_new) || !aligned16(v_new))
+    return ODA_ERR_INVALID_ARG;
+  st = check_kv(c.plan, kv, true, true);
+  if (st != ODA_OK) return st;
+  if (batch == 0) return ODA_OK;
+  const Plan& p = c.plan;
+  const int64_t q_layer = (int64_t)batch * p.Hq * p.D * p.esize;
+  const int64_t kv_layer = (int64_t)batch * p.Hkv * p.D * p.esize;
+  const int64_t o_layer = (int64_t)batch * p.Hq * p.D;
+  const int64_t l_layer = (int64_t)batch * p.Hq;
+  const void* qf = q_full ? q_full : q_local;
+  auto at = [](const void* base, int64_t off) { return static_cast<const char*>(base) + off; };
+  // 1) Local pass, every layer.
+  for (int32_t l = 0; l < p.L; ++l) {
+    st = run_pass(c, kv, l, batch, false, at(q_local, l * q_layer), at(k_new, l * kv_layer),
+                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
+                  nullptr, nullptr, stream);
+    if (st != ODA_OK) return st;
+  }
+  // 2) Gate: compaction of the fired requests, counters.
+  int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
+  int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
+  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, full_calls, counters, stream);
+  if (rc) return ODA_ERR_HIP;
+  // 3) Full recomputation of every layer for the fired requests.
+  for (int32_t l = 0; l < p.L; ++l) {
+    st = run_pass(c, kv, l, batch, true, at(qf, l * q_layer), at(k_new, l * kv_layer),
+                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
+                  list, count, stream);
+    if (st != ODA_OK) return st;
+  }
+  // 4) Fused commit of position t for all layers.
+  return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new, c.err, stream));
+}
+
+oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t b,
+                          int32_t mode, int32_t* positions, int64_t capacity, int64_t* count,
+                          void* workspace, size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, 0, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (layer < 0 || layer >= c.plan.L || b < 0 || b >= c.plan.max_batch) return ODA_ERR_INVALID_ARG;
+  if ((mode != 0 && mode != 1) || !positions || capacity < 1 || !count) return ODA_ERR_INVALID_ARG;
+  if (!kv || !kv->seq_len) return ODA_ERR_INVALID_ARG;
+  if (c.plan.focus && c.plan.kind[layer] == ODA_LAYER_GATED && mode == 1 && !kv->focus_range)
+    return ODA_ERR_INVALID_ARG;
+  return hip_status(oda::launch_access_set(c.plan, *kv, layer, b, mode, positions, capacity, count,
+                                           c.err, stream));
+}
+
+oda_status oda_stage_step(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
+                          const int64_t* step_counter, int64_t num_steps, oda_stream stream) {
+  if (n < 1 || n > 8 || !src || !dst || !bytes || !step_counter || num_steps < 1) return ODA_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    if (!src[i] || !dst[i] || bytes[i] < 16 || bytes[i] % 16 != 0) return ODA_ERR_INVALID_ARG;
+    if (!aligned16(src[i]) || !aligned16(dst[i])) return ODA_ERR_INVALID_ARG;
+  }
+  return hip_status(oda::launch_stage(n, src, dst, bytes, step_counter, num_steps, stream));
+}
+
+oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream) {
+  if (!step_counter) return ODA_ERR_INVALID_ARG;
+  return hip_status(oda::launch_advance(step_counter, stream));
+}
+
+const char* oda_status_string(oda_status status) {
+  switch (status) {
+    case ODA_OK: return "ODA_OK";
+    case ODA_ERR_INVALID_ARG: return "ODA_ERR_INVALID_ARG";
+    case ODA_ERR_UNSUPPORTED: return "ODA_ERR_UNSUPPORTED";
+    case ODA_ERR_HIP: return "ODA_ERR_HIP";
+    case ODA_ERR_WORKSPACE: return "ODA_ERR_WORKSPACE";
+  }
+  return "ODA_UNKNOWN_STATUS";
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// oda_internal.h -- plan and kernel-parameter structs shared by the host API
+// (oda_api.cpp) and the kernels (oda_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oda.h"
+
+namespace oda {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kGroupThreads = kWave * kWavesPerGroup;
+constexpr size_t kWsHeader = 256;  // error word, call count, spare
+
+// Attention passes read their rows either from a ring (Local passes and all
+// passes of sliding layers) or from the paged cache (Full / focus passes).
+enum Source : int32_t { kSrcRing = 0, kSrcPaged = 1 };
+
+// Everything the host derives once from oda_dims.
+struct Plan {
+  int32_t L, Hq, Hkv, D, G, dtype, esize;
+  int32_t sink, window, sw_window, ring_slots;  // ring_slots = sink + window
+  int32_t block_size, block_shift, max_batch, max_blocks;
+  int32_t focus;
+  int32_t Lg, Ls;
+  uint8_t kind[ODA_MAX_LAYERS];
+  int16_t kidx[ODA_MAX_LAYERS];  // rank of the layer among layers of its kind
+  int32_t full_splits, local_splits, sw_splits;
+  int32_t tile_rows;  // rows one workgroup consumes per iteration
+  float scale_log2;   // softmax scale * log2(e)
+  int64_t recall_flops;
+};
+
+// Workspace carve-up for `batch` requests.
+struct WsLayout {
+  size_t err_off, count_off, list_off, part_o_off, part_ml_off, total;
+  int32_t max_splits;
+};
+
+// Which rows a pass scans and how they map to positions.
+struct RowSpec {
+  int32_t source;        // Source
+  int32_t focus;         // paged source only: rows are S^L_t U [a,b) minus t
+  int32_t sink, window;  // ring mapping (sliding rings: sink 0, window sw)
+  int32_t ring_slots;
+};
+
+struct AttnParams {
+  RowSpec rows;
+  int32_t Hq, Hkv, splits, tile_rows;
+  int32_t max_blocks, block_shift;
+  int64_t num_blocks;
+  const void* k_base;  // ring of this layer: [max_batch][Hkv][slots][d]; or cache layer base
+  const void* v_base;
+  const int32_t* block_table;
+  const int32_t* seq_len;
+  const int64_t* focus_range;
+  const int32_t* call_list;   // NULL: blockIdx.z is the request id
+  const int32_t* call_count;
+  const void* q;              // [batch][Hq][d]
+  float* part_o;              // [batch][Hq][splits][d]
+  float* part_ml;             // [batch][Hq][splits][2]
+  uint32_t* err;
+  float scale_log2;
+  int32_t capacity;           // max_blocks * block_size
+};
+
+struct MergeParams {
+  RowSpec rows;
+  int32_t Hq, Hkv, splits, tile_rows, capacity;
+  const int32_t* seq_len;
+  const int64_t* focus_range;
+  const int32_t* call_list;
+  const int32_t* call_count;
+  const void* q;       // [batch][Hq][d]
+  const void* k_cur;   // [batch][Hkv][d]
+  const void* v_cur;
+  const float* part_o;
+  const float* part_ml;
+  float* out;          // [batch][Hq][d]
+  float* lse;          // [batch][Hq] or NULL
+  float scale_log2;
+};
+
+// Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
+int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
+int launch_merge(const Plan& p, const MergeParams& m, int32_t batch, oda_stream s);
+int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
+                int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                oda_stream s);
+int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
+                  const void* v_new, uint32_t* err, oda_stream s);
+int launch_prefill(const Plan& p, const oda_kv& kv, int32_t batch, int32_t layer,
+                   const void* k_src, const void* v_src, int64_t src_rows, uint32_t* err,
+                   oda_stream s);
+int launch_ring_init(const Plan& p, const oda_kv& kv, int32_t batch, uint32_t* err, oda_stream s);
+int launch_access_set(const Plan& p, const oda_kv& kv, int32_t layer, int32_t b, int32_t mode,
+                      int32_t* positions, int64_t capacity, int64_t* count, uint32_t* err,
+                      oda_stream s);
+int launch_clear(void* ptr, size_t bytes, oda_stream s);
+int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
+                 const int64_t* counter, int64_t num_steps, oda_stream s);
+int launch_advance(int64_t* counter, oda_stream s);
+// Rows per workgroup iteration for the attention kernel built for (dtype, d).
+int tile_rows_for(int32_t dtype, int32_t head_dim);
+
+}  // namespace oda

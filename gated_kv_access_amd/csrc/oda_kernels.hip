@@ -1,0 +1,1167 @@
+// oda_kernels.hip -- gfx950 (CDNA4) kernels of the On-Demand Attention decode
+// step and their launchers.
+//
+// Method: picx.dev summary of "On-Demand Attention", section "Local-First
+// Decoding" (access sets S^L_t, S^F_t; Local pass; gate q_t > theta) and
+// section "Efficient Execution" (ring KV workspace, fused cross-layer commits,
+// device-side conditional Full pass).
+//
+// Attention is split-K flash decoding.  A workgroup of four wave64s owns one
+// (split, KV head, request) and streams its rows of K and V with 16-byte
+// loads: every lane holds 64 contiguous-in-chunks bytes of a row, so a row of
+// 256 bytes (bf16, d = 128) is spread over 4 lanes and one wave covers 16 rows
+// per pass.  Both query heads of a GQA group use each loaded row.  Scores are
+// reduced across the lanes of a row with DPP, the running maximum is kept per
+// wave (log2 domain, fp32), and each workgroup leaves one (o, m, l) partial per
+// query head; a merge kernel folds the partials and the current token.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "oda_internal.h"
+
+namespace oda {
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// ----------------------------------------------------------------------------
+// lane exchange
+
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (MASK == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (MASK == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (MASK < 32) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10)));      // xor within 32
+  } else {
+    return __shfl_xor(v, MASK, 64);
+  }
+}
+
+template <int FIRST, int LAST>
+__device__ __forceinline__ float sum_over(float v) {
+  if constexpr (FIRST > LAST) {
+    return v;
+  } else {
+    v += xor_lane<FIRST>(v);
+    return sum_over<FIRST * 2, LAST>(v);
+  }
+}
+
+template <int FIRST, int LAST>
+__device__ __forceinline__ float max_over(float v) {
+  if constexpr (FIRST > LAST) {
+    return v;
+  } else {
+    v = fmaxf(v, xor_lane<FIRST>(v));
+    return max_over<FIRST * 2, LAST>(v);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ----------------------------------------------------------------------------
+// element formats
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int DT, int D>
+struct Geo {
+  static constexpr int ES = DT == ODA_BF16 ? 2 : 4;
+  static constexpr int ROW_BYTES = D * ES;
+  static constexpr int LPR = ROW_BYTES / 64;  // lanes sharing a row
+  static constexpr int RPP = kWave / LPR;     // rows per wave pass
+  static constexpr int EPV = 16 / ES;         // elements per 16-byte vector
+  static constexpr int EPL = 4 * EPV;         // elements per lane per row
+  static constexpr int NP = 2;                // passes per wave per tile
+  static constexpr int TILE = kWavesPerGroup * NP * RPP;
+  static_assert(LPR >= 2 && LPR <= 8, "row must span 2..8 lanes");
+};
+
+// ----------------------------------------------------------------------------
+// access-set index code (shared by every kernel that turns rows into positions)
+
+// Ring state of a request just before decoding position t (1..t-1 committed).
+struct RingState {
+  int32_t t, s, w;
+  int32_t c;     // latest committed position (t - 1)
+  int32_t r;     // window slot offset of position c, valid when c > s
+};
+
+__device__ __forceinline__ RingState ring_state(int32_t t, int32_t s, int32_t w) {
+  RingState st;
+  st.t = t;
+  st.s = s;
+  st.w = w;
+  st.c = t - 1;
+  st.r = st.c > s ? (st.c - s - 1) % w : 0;
+  return st;
+}
+
+// Position the one-by-one commits left in slot j (0 if none), and whether it
+// belongs to the Local set of t.  Window slot k = j - s holds the latest
+// committed position p > s with (p - s - 1) mod w == k.
+__device__ __forceinline__ int32_t ring_slot_position(const RingState& st, int32_t j, bool& in_local) {
+  if (j < st.s) {
+    const int32_t p = j + 1;
+    in_local = p <= st.c;
+    return in_local ? p : 0;
+  }
+  if (st.c <= st.s) {
+    in_local = false;
+    return 0;
+  }
+  int32_t back = st.r - (j - st.s);
+  if (back < 0) back += st.w;
+  const int32_t p = st.c - back;
+  if (p <= st.s) {
+    in_local = false;
+    return 0;
+  }
+  in_local = p >= st.t - st.w + 1;  // excludes only position t - w
+  return p;
+}
+
+// Rows a ring pass scans: the filled prefix of the ring.
+__device__ __forceinline__ int32_t ring_rows(int32_t t, int32_t slots) {
+  return min(slots, t - 1);
+}
+
+// Positions a paged pass reads (the current token t excluded), as up to three
+// disjoint ascending closed intervals.
+struct Intervals {
+  int32_t lo[3];
+  int32_t n[3];
+  int32_t total;
+};
+
+__device__ __forceinline__ Intervals paged_intervals(const RowSpec& rs, int32_t t, int64_t fa, int64_t fb) {
+  Intervals iv;
+  const int32_t last = t - 1;
+  if (!rs.focus) {
+    iv.lo[0] = 1;
+    iv.n[0] = max(last, 0);
+    iv.lo[1] = iv.lo[2] = 1;
+    iv.n[1] = iv.n[2] = 0;
+    iv.total = iv.n[0];
+    return iv;
+  }
+  // S^L_t U [a, b), minus t: sinks, focus region, window -- then sort and merge.
+  int32_t lo[3], hi[3];
+  lo[0] = 1;
+  hi[0] = min(rs.sink, last);
+  const int64_t a = fa < 1 ? 1 : fa;
+  const int64_t bb = (fb - 1) < last ? (fb - 1) : last;
+  lo[1] = (int32_t)(a > (int64_t)last + 1 ? (int64_t)last + 1 : a);
+  hi[1] = (int32_t)(bb < 0 ? 0 : bb);
+  lo[2] = max(1, t - rs.window + 1);
+  hi[2] = last;
+  for (int i = 0; i < 3; ++i)
+    for (int k = 0; k + 1 < 3 - i; ++k)
+      if (lo[k] > lo[k + 1]) {
+        int32_t x = lo[k]; lo[k] = lo[k + 1]; lo[k + 1] = x;
+        x = hi[k]; hi[k] = hi[k + 1]; hi[k + 1] = x;
+      }
+  int32_t m = 0;
+  int32_t mlo[3], mhi[3];
+  for (int k = 0; k < 3; ++k) {
+    if (hi[k] < lo[k]) continue;  // empty
+    if (m > 0 && lo[k] <= mhi[m - 1] + 1) {
+      mhi[m - 1] = max(mhi[m - 1], hi[k]);
+    } else {
+      mlo[m] = lo[k];
+      mhi[m] = hi[k];
+      ++m;
+    }
+  }
+  iv.total = 0;
+  for (int k = 0; k < 3; ++k) {
+    if (k < m) {
+      iv.lo[k] = mlo[k];
+      iv.n[k] = mhi[k] - mlo[k] + 1;
+    } else {
+      iv.lo[k] = 1;
+      iv.n[k] = 0;
+    }
+    iv.total += iv.n[k];
+  }
+  return iv;
+}
+
+__device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_t row) {
+  if (row < iv.n[0]) return iv.lo[0] + row;
+  row -= iv.n[0];
+  if (row < iv.n[1]) return iv.lo[1] + row;
+  row -= iv.n[1];
+  return iv.lo[2] + row;
+}
+
+__device__ __forceinline__ int32_t pass_rows(const RowSpec& rs, int32_t t, const int64_t* focus_range,
+                                             int32_t b) {
+  if (rs.source == kSrcRing) return ring_rows(t, rs.ring_slots);
+  int64_t fa = 0, fb = 0;
+  if (rs.focus) {
+    fa = focus_range[2 * b];
+    fb = focus_range[2 * b + 1];
+  }
+  return paged_intervals(rs, t, fa, fb).total;
+}
+
+// Splitting n_rows over `splits` workgroups in whole tiles.
+__device__ __forceinline__ void split_tiles(int32_t n_rows, int32_t tile, int32_t splits, int32_t& per,
+                                            int32_t& used) {
+  const int32_t n_tiles = (n_rows + tile - 1) / tile;
+  per = (n_tiles + splits - 1) / splits;
+  if (per < 1) per = 1;
+  used = (n_tiles + per - 1) / per;
+}
+
+// Request handled by blockIdx.z (or merge blockIdx.y): compacted call list or identity.
+__device__ __forceinline__ int32_t request_of(int32_t slot, const int32_t* call_list,
+                                              const int32_t* call_count) {
+  if (call_list == nullptr) return slot;
+  if (slot >= *call_count) return -1;
+  return call_list[slot];
+}
+
+// ----------------------------------------------------------------------------
+// split-K partial attention
+
+template <int DT, int D, int G, int SRC>
+__global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnParams P) {
+  using Gm = Geo<DT, D>;
+  constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
+  constexpr int TILE = Gm::TILE;
+  constexpr int ES = Gm::ES;
+
+  const int32_t b = request_of(blockIdx.z, P.call_list, P.call_count);
+  if (b < 0) return;
+  const int32_t committed = P.seq_len[b];
+  if (committed < 0) return;
+  const int32_t t = committed + 1;
+  if (SRC == kSrcPaged && t - 1 > P.capacity) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+    return;
+  }
+  const int32_t g = blockIdx.y;
+  const int32_t split = blockIdx.x;
+
+  RingState rst{};
+  Intervals iv{};
+  int32_t n_rows;
+  if constexpr (SRC == kSrcRing) {
+    rst = ring_state(t, P.rows.sink, P.rows.window);
+    n_rows = ring_rows(t, P.rows.ring_slots);
+  } else {
+    int64_t fa = 0, fb = 0;
+    if (P.rows.focus) {
+      fa = P.focus_range[2 * b];
+      fb = P.focus_range[2 * b + 1];
+    }
+    iv = paged_intervals(P.rows, t, fa, fb);
+    n_rows = iv.total;
+  }
+  int32_t per, used;
+  split_tiles(n_rows, TILE, P.splits, per, used);
+  if (split >= used) return;
+  const int32_t tile_begin = split * per;
+  const int32_t tile_end = min(tile_begin + per, (n_rows + TILE - 1) / TILE);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int rrow = lane / LPR;
+
+  // Query heads g*G .. g*G+G-1, in this lane's element slots.
+  uint4 qv[G][4];
+  {
+    const char* qbase = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + (int64_t)g * G) * D * ES;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qv[h][j] = *reinterpret_cast<const uint4*>(qbase + (int64_t)h * D * ES + (j * LPR + sub) * 16);
+  }
+
+  const char* kbase = static_cast<const char*>(P.k_base);
+  const char* vbase = static_cast<const char*>(P.v_base);
+  int64_t ring_head_off = 0;
+  if constexpr (SRC == kSrcRing)
+    ring_head_off = (((int64_t)b * P.Hkv + g) * P.rows.ring_slots) * D * ES;
+  const int32_t* btab = P.block_table + (int64_t)b * P.max_blocks;
+  const int32_t bmask = (1 << P.block_shift) - 1;
+
+  float m_run[G], l_acc[G], o[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_acc[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+  }
+
+  for (int32_t tile = tile_begin; tile < tile_end; ++tile) {
+    uint4 kr[NP][4], vr[NP][4];
+    bool valid[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
+      bool ok = row < n_rows;
+      int64_t off = 0;
+      if constexpr (SRC == kSrcRing) {
+        if (ok) {
+          bool in_local;
+          ring_slot_position(rst, row, in_local);
+          ok = in_local;
+          off = ring_head_off + (int64_t)row * D * ES;
+        }
+      } else {
+        if (ok) {
+          const int32_t p = interval_position(iv, row);
+          const int32_t r0 = p - 1;
+          const int32_t blk = btab[r0 >> P.block_shift];
+          if (blk < 0 || (int64_t)blk >= P.num_blocks) {
+            atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
+            ok = false;
+          } else {
+            off = ((((int64_t)blk * P.Hkv + g) << P.block_shift) + (r0 & bmask)) * D * ES;
+          }
+        }
+      }
+      valid[i] = ok;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ok) {
+          kr[i][j] = *reinterpret_cast<const uint4*>(kbase + off + (j * LPR + sub) * 16);
+          vr[i][j] = *reinterpret_cast<const uint4*>(vbase + off + (j * LPR + sub) * 16);
+        } else {
+          kr[i][j] = make_uint4(0, 0, 0, 0);
+          vr[i][j] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+
+    // scores s = scale*log2(e) * <q_h, k_row>
+    float s[NP][G];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 kk = kr[i][j];
+          const uint4 qq = qv[h][j];
+          if constexpr (DT == ODA_BF16) {
+            acc = dot2_bf16(kk.x, qq.x, acc);
+            acc = dot2_bf16(kk.y, qq.y, acc);
+            acc = dot2_bf16(kk.z, qq.z, acc);
+            acc = dot2_bf16(kk.w, qq.w, acc);
+          } else {
+            acc = fmaf(__uint_as_float(kk.x), __uint_as_float(qq.x), acc);
+            acc = fmaf(__uint_as_float(kk.y), __uint_as_float(qq.y), acc);
+            acc = fmaf(__uint_as_float(kk.z), __uint_as_float(qq.z), acc);
+            acc = fmaf(__uint_as_float(kk.w), __uint_as_float(qq.w), acc);
+          }
+        }
+        acc = sum_over<1, LPR / 2>(acc);
+        s[i][h] = valid[i] ? acc * P.scale_log2 : -INFINITY;
+      }
+    }
+
+    // running maximum per head, uniform over the wave
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float tm = s[0][h];
+#pragma unroll
+      for (int i = 1; i < NP; ++i) tm = fmaxf(tm, s[i][h]);
+      tm = max_over<LPR, 32>(tm);
+      const float m_new = fmaxf(m_run[h], tm);
+      if (m_new > m_run[h]) {
+        const float alpha = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - m_new);
+        l_acc[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        m_run[h] = m_new;
+      }
+    }
+
+    // p = exp2(s - m); o += p * v
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float pr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pr[h] = valid[i] ? fast_exp2(s[i][h] - m_run[h]) : 0.f;
+        l_acc[h] += pr[h];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w4[4] = {vr[i][j].x, vr[i][j].y, vr[i][j].z, vr[i][j].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (DT == ODA_BF16) {
+            const float v0 = bf16_lo(w4[c]);
+            const float v1 = bf16_hi(w4[c]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              o[h][j * EPV + 2 * c] = fmaf(pr[h], v0, o[h][j * EPV + 2 * c]);
+              o[h][j * EPV + 2 * c + 1] = fmaf(pr[h], v1, o[h][j * EPV + 2 * c + 1]);
+            }
+          } else {
+            const float v0 = __uint_as_float(w4[c]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) o[h][j * EPV + c] = fmaf(pr[h], v0, o[h][j * EPV + c]);
+          }
+        }
+      }
+    }
+  }
+
+  // wave epilogue: fold the row groups (lanes that share `sub`)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l_acc[h] = sum_over<LPR, 32>(l_acc[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = sum_over<LPR, 32>(o[h][e]);
+  }
+
+  __shared__ float s_o[kWavesPerGroup][G][D];
+  __shared__ float s_m[kWavesPerGroup][G];
+  __shared__ float s_l[kWavesPerGroup][G];
+  if (rrow == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < EPV; ++c) s_o[wave][h][(j * LPR + sub) * EPV + c] = o[h][j * EPV + c];
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_m[wave][h] = m_run[h];
+        s_l[wave][h] = l_acc[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
+    const int h = idx / D, e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) M = fmaxf(M, s_m[w][h]);
+    float acc = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerGroup; ++w) {
+        const float sc = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - M);
+        acc = fmaf(sc, s_o[w][h][e], acc);
+        lsum = fmaf(sc, s_l[w][h], lsum);
+      }
+    }
+    const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
+    P.part_o[row * D + e] = acc;
+    if (e == 0) {
+      P.part_ml[row * 2 + 0] = M;
+      P.part_ml[row * 2 + 1] = lsum;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// log-sum-exp merge of the partials and the current token
+
+template <int DT, int D>
+__global__ __launch_bounds__(kWave) void merge_kernel(MergeParams P) {
+  constexpr int ES = DT == ODA_BF16 ? 2 : 4;
+  constexpr int EPT = D / kWave;  // elements per lane (1 or 2)
+  const int32_t b = request_of(blockIdx.y, P.call_list, P.call_count);
+  if (b < 0) return;
+  const int32_t committed = P.seq_len[b];
+  if (committed < 0) return;
+  const int32_t t = committed + 1;
+  if (P.rows.source == kSrcPaged && t - 1 > P.capacity) return;
+  const int32_t h = blockIdx.x;
+  const int32_t g = h / (P.Hq / P.Hkv);
+  const int lane = threadIdx.x;
+
+  const int32_t n_rows = pass_rows(P.rows, t, P.focus_range, b);
+  int32_t per, used;
+  split_tiles(n_rows, P.tile_rows, P.splits, per, used);
+  if (n_rows == 0) used = 0;
+
+  float qx[EPT], kx[EPT], vx[EPT];
+  const char* qrow = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + h) * D * ES;
+  const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+  const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) {
+    const int e = lane * EPT + c;
+    if constexpr (DT == ODA_BF16) {
+      qx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[e] << 16);
+      kx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[e] << 16);
+      vx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
+    } else {
+      qx[c] = reinterpret_cast<const float*>(qrow)[e];
+      kx[c] = reinterpret_cast<const float*>(krow)[e];
+      vx[c] = reinterpret_cast<const float*>(vrow)[e];
+    }
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) dot = fmaf(qx[c], kx[c], dot);
+  dot = sum_over<1, 32>(dot);
+  const float s_cur = dot * P.scale_log2;
+
+  const int64_t row0 = ((int64_t)b * P.Hq + h) * P.splits;
+  float M = s_cur;
+  for (int i = 0; i < used; ++i) M = fmaxf(M, P.part_ml[(row0 + i) * 2]);
+  float lsum = fast_exp2(s_cur - M);
+  float acc[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) acc[c] = lsum * vx[c];
+  for (int i = 0; i < used; ++i) {
+    const float mi = P.part_ml[(row0 + i) * 2];
+    const float li = P.part_ml[(row0 + i) * 2 + 1];
+    const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+    lsum = fmaf(w, li, lsum);
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) acc[c] = fmaf(w, P.part_o[(row0 + i) * D + lane * EPT + c], acc[c]);
+  }
+  const float inv = 1.f / lsum;
+  float* orow = P.out + ((int64_t)b * P.Hq + h) * D;
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) orow[lane * EPT + c] = acc[c] * inv;
+  if (P.lse != nullptr && lane == 0) P.lse[(int64_t)b * P.Hq + h] = (M + __log2f(lsum)) * kLn2;
+}
+
+// ----------------------------------------------------------------------------
+// gate: compaction of the fired requests + accounting
+
+struct GateParams {
+  int32_t batch, L, Hq, Hkv, D, esize, sink, window, sw_window, focus;
+  int32_t n_gated, n_sliding;
+  int64_t recall_flops;
+  const float* score;
+  float theta;
+  const int32_t* seq_len;
+  const int64_t* focus_range;
+  int32_t* call_list;
+  int32_t* call_count;
+  int64_t* full_calls;
+  int64_t* counters;
+};
+
+// Size of S^L_t U [a,b) (closed form over the merged intervals, plus t).
+__device__ int64_t focus_set_size(int32_t t, int32_t s, int32_t w, int64_t fa, int64_t fb) {
+  RowSpec rs{};
+  rs.source = kSrcPaged;
+  rs.focus = 1;
+  rs.sink = s;
+  rs.window = w;
+  return (int64_t)paged_intervals(rs, t, fa, fb).total + 1;
+}
+
+__global__ __launch_bounds__(1024) void gate_kernel(GateParams P) {
+  __shared__ int32_t s_wave_count[1024 / kWave];
+  __shared__ int32_t s_base;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  if (threadIdx.x == 0) s_base = 0;
+  __syncthreads();
+  for (int32_t start = 0; start < P.batch; start += blockDim.x) {
+    const int32_t b = start + threadIdx.x;
+    bool fire = false;
+    int32_t t = 0;
+    if (b < P.batch) {
+      const int32_t committed = P.seq_len[b];
+      t = committed + 1;
+      fire = committed >= 0 && P.score[b] > P.theta;  // NaN compares false
+      if (committed >= 0) {
+        if (P.full_calls) P.full_calls[b] += fire ? 1 : 0;
+        if (P.counters) {
+          const int64_t per_pos = 4LL * P.Hq * P.D;
+          const int64_t bytes_pos = (int64_t)P.Hkv * P.D * 2 * P.esize;
+          const int64_t nl_g = min(t, P.sink + P.window);
+          int64_t nf_g = t;
+          if (P.focus) nf_g = focus_set_size(t, P.sink, P.window, P.focus_range[2 * b], P.focus_range[2 * b + 1]);
+          const int64_t n_sw = P.n_sliding > 0 ? min(t, P.sw_window) : 0;
+          const int64_t nl = P.n_gated * nl_g + P.n_sliding * n_sw;
+          const int64_t nf = P.n_gated * nf_g + P.n_sliding * n_sw;
+          const int64_t f_local = per_pos * nl, f_full = per_pos * nf;
+          int64_t* c = P.counters + (int64_t)b * ODA_ACCT_N;
+          c[ODA_ACCT_STEPS] += 1;
+          c[ODA_ACCT_FULL_CALLS] += fire ? 1 : 0;
+          c[ODA_ACCT_F_LOCAL] += f_local;
+          c[ODA_ACCT_F_FULL_TAKEN] += fire ? f_full : 0;
+          c[ODA_ACCT_F_FULL_ALWAYS] += f_full;
+          c[ODA_ACCT_DELTA_F] += (fire ? 0 : f_full) - f_local - P.recall_flops;
+          c[ODA_ACCT_KV_BYTES] += bytes_pos * (nl + (fire ? nf : 0));
+          c[ODA_ACCT_F_RECALL] += P.recall_flops;
+        }
+      }
+    }
+    const uint64_t ballot = __ballot(fire);
+    if (lane == 0) s_wave_count[wave] = __popcll(ballot);
+    __syncthreads();
+    int32_t before = s_base;
+    for (int w = 0; w < wave; ++w) before += s_wave_count[w];
+    const uint64_t lower = lane == 0 ? 0ull : (ballot & ((1ull << lane) - 1ull));
+    if (fire && P.call_list) P.call_list[before + __popcll(lower)] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int32_t total = 0;
+      for (int w = 0; w < nwaves; ++w) total += s_wave_count[w];
+      s_base += total;
+    }
+    __syncthreads();
+  }
+  const int32_t count = s_base;
+  if (P.call_list)
+    for (int32_t i = count + threadIdx.x; i < P.batch; i += blockDim.x) P.call_list[i] = -1;
+  if (threadIdx.x == 0 && P.call_count) *P.call_count = count;
+}
+
+// ----------------------------------------------------------------------------
+// fused cross-layer commit
+
+struct CommitParams {
+  int32_t L, Hkv, D, esize, sink, window, ring_slots, sw_window, block_shift, max_blocks;
+  int32_t batch, ring_batch;
+  int64_t num_blocks;
+  int32_t n_layers_gated, n_layers_sliding;
+  uint8_t kind[ODA_MAX_LAYERS];
+  int16_t kidx[ODA_MAX_LAYERS];
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* k_ring;
+  void* v_ring;
+  void* k_swring;
+  void* v_swring;
+  int32_t* ring_pos;
+  int32_t* swring_pos;
+  const int32_t* block_table;
+  int32_t* seq_len;
+  uint32_t* err;
+};
+
+__global__ __launch_bounds__(256) void commit_kernel(CommitParams P) {
+  const int32_t b = blockIdx.x;
+  if (b >= P.batch) return;
+  const int32_t committed = P.seq_len[b];
+  if (committed < 0) return;
+  const int32_t t = committed + 1;
+  const int64_t cap = (int64_t)P.max_blocks << P.block_shift;
+  const bool has_gated = P.n_layers_gated > 0;
+  if (has_gated && t > cap) {
+    if (threadIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+    return;
+  }
+  int32_t blk = 0;
+  if (has_gated) {
+    blk = P.block_table[(int64_t)b * P.max_blocks + ((t - 1) >> P.block_shift)];
+    if (blk < 0 || (int64_t)blk >= P.num_blocks) {
+      if (threadIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
+      return;
+    }
+  }
+  const int32_t in_blk = (t - 1) & ((1 << P.block_shift) - 1);
+  const int32_t gslot = t <= P.sink ? t - 1 : P.sink + (t - P.sink - 1) % P.window;
+  const int32_t sslot = P.sw_window > 0 ? (t - 1) % P.sw_window : 0;
+  const int64_t row_bytes = (int64_t)P.D * P.esize;
+  const int32_t vecs = (int32_t)(row_bytes / 16);
+  const int32_t per_layer = P.Hkv * vecs;
+
+  for (int32_t idx = threadIdx.x; idx < P.L * per_layer; idx += blockDim.x) {
+    const int32_t l = idx / per_layer;
+    const int32_t rem = idx % per_layer;
+    const int32_t h = rem / vecs, vi = rem % vecs;
+    const int64_t src = (((int64_t)l * P.batch + b) * P.Hkv + h) * row_bytes + vi * 16;
+    const uint4 kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_new) + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_new) + src);
+    const int64_t rank = P.kidx[l];
+    if (P.kind[l] == ODA_LAYER_GATED) {
+      const int64_t coff = ((((rank * P.num_blocks + blk) * P.Hkv + h) << P.block_shift) + in_blk) * row_bytes + vi * 16;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.k_cache) + coff) = kx;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.v_cache) + coff) = vx;
+      const int64_t roff = (((rank * P.ring_batch + b) * P.Hkv + h) * P.ring_slots + gslot) * row_bytes + vi * 16;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.k_ring) + roff) = kx;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.v_ring) + roff) = vx;
+    } else {
+      const int64_t roff = (((rank * P.ring_batch + b) * P.Hkv + h) * P.sw_window + sslot) * row_bytes + vi * 16;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.k_swring) + roff) = kx;
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.v_swring) + roff) = vx;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (has_gated) P.ring_pos[(int64_t)b * P.ring_slots + gslot] = t;
+    if (P.n_layers_sliding > 0) P.swring_pos[(int64_t)b * P.sw_window + sslot] = t;
+    P.seq_len[b] = t;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// prefill of one layer from a dense source, and ring rebuild from the cache
+
+struct PrefillParams {
+  int32_t Hkv, D, esize, gated, sink, window, slots, block_shift, max_blocks;
+  int64_t num_blocks, src_rows;
+  int32_t rank;      // layer rank among its kind
+  int32_t ring_batch;  // request stride of rings (max_batch)
+  const void* k_src;
+  const void* v_src;
+  void* k_cache;
+  void* v_cache;
+  void* k_ring;
+  void* v_ring;
+  int32_t* ring_pos;
+  const int32_t* block_table;
+  const int32_t* seq_len;
+  uint32_t* err;
+  int32_t from_cache;  // ring rebuild: read rows from the paged cache instead of src
+};
+
+// grid (x: row chunks, y: request); rows of the paged cache then ring slots
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
+  const int32_t b = blockIdx.y;
+  const int32_t committed = P.seq_len[b];
+  if (committed < 0) return;
+  const int64_t row_bytes = (int64_t)P.D * P.esize;
+  const int32_t vecs = (int32_t)(row_bytes / 16);
+  const int64_t cap = (int64_t)P.max_blocks << P.block_shift;
+  const int32_t bmask = (1 << P.block_shift) - 1;
+  if (P.gated && committed > cap) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+    return;
+  }
+  if (!P.from_cache && committed > P.src_rows) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+    return;
+  }
+  const int32_t* btab = P.block_table + (int64_t)b * P.max_blocks;
+  auto cache_off = [&](int32_t p, int32_t h, int32_t vi, bool& ok) -> int64_t {
+    const int32_t r0 = p - 1;
+    const int32_t blk = btab[r0 >> P.block_shift];
+    ok = blk >= 0 && (int64_t)blk < P.num_blocks;
+    return (((((int64_t)P.rank * P.num_blocks + blk) * P.Hkv + h) << P.block_shift) + (r0 & bmask)) * row_bytes + vi * 16;
+  };
+  auto src_off = [&](int32_t p, int32_t h, int32_t vi) -> int64_t {
+    return ((((int64_t)b * P.src_rows + (p - 1)) * P.Hkv + h) * row_bytes) + vi * 16;
+  };
+  const int64_t per_row = (int64_t)P.Hkv * vecs;
+  // 1) paged cache rows 1..committed (gated layers, dense source only)
+  if (P.gated && !P.from_cache) {
+    const int64_t total = (int64_t)committed * per_row;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+      const int32_t p = (int32_t)(idx / per_row) + 1;
+      const int32_t rem = (int32_t)(idx % per_row);
+      const int32_t h = rem / vecs, vi = rem % vecs;
+      bool ok;
+      const int64_t co = cache_off(p, h, vi, ok);
+      if (!ok) {
+        atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
+        continue;
+      }
+      const int64_t so = src_off(p, h, vi);
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.k_cache) + co) =
+          *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_src) + so);
+      *reinterpret_cast<uint4*>(static_cast<char*>(P.v_cache) + co) =
+          *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_src) + so);
+    }
+  }
+  // 2) ring slots: the state a one-by-one commit of 1..committed leaves
+  const RingState st = ring_state(committed + 1, P.sink, P.window);
+  const int64_t total_slots = (int64_t)P.slots * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total_slots;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t j = (int32_t)(idx / per_row);
+    const int32_t rem = (int32_t)(idx % per_row);
+    const int32_t h = rem / vecs, vi = rem % vecs;
+    bool in_local;
+    const int32_t p = ring_slot_position(st, j, in_local);
+    if (h == 0 && vi == 0) P.ring_pos[(int64_t)b * P.slots + j] = p;
+    if (p == 0) continue;
+    const int64_t ro = ((((int64_t)P.rank * P.ring_batch + b) * P.Hkv + h) * P.slots + j) * row_bytes + vi * 16;
+    uint4 kx, vx;
+    if (P.from_cache) {
+      bool ok;
+      const int64_t co = cache_off(p, h, vi, ok);
+      if (!ok) {
+        atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
+        continue;
+      }
+      kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_cache) + co);
+      vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_cache) + co);
+    } else {
+      const int64_t so = src_off(p, h, vi);
+      kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_src) + so);
+      vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_src) + so);
+    }
+    *reinterpret_cast<uint4*>(static_cast<char*>(P.k_ring) + ro) = kx;
+    *reinterpret_cast<uint4*>(static_cast<char*>(P.v_ring) + ro) = vx;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// access-set export
+
+struct AccessParams {
+  RowSpec rows;
+  int32_t b, capacity_rows, block_shift, max_blocks;
+  const int32_t* seq_len;
+  const int64_t* focus_range;
+  int32_t* positions;
+  int64_t capacity;
+  int64_t* count;
+  uint32_t* err;
+};
+
+__global__ __launch_bounds__(256) void access_set_kernel(AccessParams P) {
+  __shared__ int32_t s_count;
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  const int32_t committed = P.seq_len[P.b];
+  if (committed >= 0) {
+    const int32_t t = committed + 1;
+    RingState rst{};
+    Intervals iv{};
+    int32_t n_rows;
+    if (P.rows.source == kSrcRing) {
+      rst = ring_state(t, P.rows.sink, P.rows.window);
+      n_rows = ring_rows(t, P.rows.ring_slots);
+    } else {
+      int64_t fa = 0, fb = 0;
+      if (P.rows.focus) {
+        fa = P.focus_range[2 * P.b];
+        fb = P.focus_range[2 * P.b + 1];
+      }
+      iv = paged_intervals(P.rows, t, fa, fb);
+      n_rows = iv.total;
+    }
+    for (int32_t row = threadIdx.x; row <= n_rows; row += blockDim.x) {
+      int32_t p;
+      if (row == n_rows) {
+        p = t;  // the current token, supplied by the caller's k_cur / v_cur
+      } else if (P.rows.source == kSrcRing) {
+        bool in_local;
+        p = ring_slot_position(rst, row, in_local);
+        if (!in_local) p = 0;
+      } else {
+        p = interval_position(iv, row);
+      }
+      if (p > 0) {
+        const int32_t at = atomicAdd(&s_count, 1);
+        if (at < P.capacity) P.positions[at] = p;
+        else atomicOr(P.err, (uint32_t)ODA_DEVERR_OUT_CAPACITY);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *P.count = s_count;
+}
+
+// ----------------------------------------------------------------------------
+// small helpers
+
+__global__ void clear_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+struct StageParams {
+  int32_t n;
+  const void* src[8];
+  void* dst[8];
+  int64_t bytes[8];
+  const int64_t* counter;
+  int64_t num_steps;
+};
+
+__global__ __launch_bounds__(256) void stage_kernel(StageParams P) {
+  const int64_t k = *P.counter % P.num_steps;
+  for (int i = 0; i < P.n; ++i) {
+    const int64_t vecs = P.bytes[i] / 16;
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const char*>(P.src[i]) + k * P.bytes[i]);
+    uint4* d = reinterpret_cast<uint4*>(P.dst[i]);
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < vecs; v += (int64_t)gridDim.x * blockDim.x)
+      d[v] = s[v];
+  }
+}
+
+__global__ void advance_kernel(int64_t* counter) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *counter += 1;
+}
+
+// ----------------------------------------------------------------------------
+// dispatch over the built instantiations
+
+template <int DT, int D, int G>
+int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
+  dim3 grid(a.splits, a.Hkv, batch);
+  if (a.rows.source == kSrcRing)
+    hipLaunchKernelGGL((attention_partial_kernel<DT, D, G, kSrcRing>), grid, dim3(kGroupThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attention_partial_kernel<DT, D, G, kSrcPaged>), grid, dim3(kGroupThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+template <int DT, int D>
+int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {
+  switch (p.G) {
+    case 1: return launch_attention_t<DT, D, 1>(a, batch, s);
+    case 2: return launch_attention_t<DT, D, 2>(a, batch, s);
+    case 4: return launch_attention_t<DT, D, 4>(a, batch, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int tile_rows_for(int32_t dtype, int32_t head_dim) {
+  if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128>::TILE : Geo<ODA_BF16, 64>::TILE;
+  return head_dim == 128 ? Geo<ODA_F32, 128>::TILE : Geo<ODA_F32, 64>::TILE;
+}
+
+int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {
+  if (batch <= 0) return 0;
+  if (p.dtype == ODA_BF16) {
+    if (p.D == 128) return launch_attention_d<ODA_BF16, 128>(p, a, batch, s);
+    return launch_attention_d<ODA_BF16, 64>(p, a, batch, s);
+  }
+  if (p.D == 128) return launch_attention_d<ODA_F32, 128>(p, a, batch, s);
+  return launch_attention_d<ODA_F32, 64>(p, a, batch, s);
+}
+
+int launch_merge(const Plan& p, const MergeParams& m, int32_t batch, oda_stream s) {
+  if (batch <= 0) return 0;
+  dim3 grid(p.Hq, batch);
+  if (p.dtype == ODA_BF16) {
+    if (p.D == 128) hipLaunchKernelGGL((merge_kernel<ODA_BF16, 128>), grid, dim3(kWave), 0, s, m);
+    else hipLaunchKernelGGL((merge_kernel<ODA_BF16, 64>), grid, dim3(kWave), 0, s, m);
+  } else {
+    if (p.D == 128) hipLaunchKernelGGL((merge_kernel<ODA_F32, 128>), grid, dim3(kWave), 0, s, m);
+    else hipLaunchKernelGGL((merge_kernel<ODA_F32, 64>), grid, dim3(kWave), 0, s, m);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
+                int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                oda_stream s) {
+  if (batch <= 0) return 0;
+  GateParams g{};
+  g.batch = batch;
+  g.L = p.L;
+  g.Hq = p.Hq;
+  g.Hkv = p.Hkv;
+  g.D = p.D;
+  g.esize = p.esize;
+  g.sink = p.sink;
+  g.window = p.window;
+  g.sw_window = p.sw_window;
+  g.focus = p.focus;
+  g.n_gated = p.Lg;
+  g.n_sliding = p.Ls;
+  g.recall_flops = p.recall_flops;
+  g.score = score;
+  g.theta = theta;
+  g.seq_len = kv.seq_len;
+  g.focus_range = kv.focus_range;
+  g.call_list = call_list;
+  g.call_count = call_count;
+  g.full_calls = full_calls;
+  g.counters = counters;
+  const int threads = batch >= 1024 ? 1024 : ((batch + 63) / 64) * 64;
+  hipLaunchKernelGGL(gate_kernel, dim3(1), dim3(threads), 0, s, g);
+  return (int)hipGetLastError();
+}
+
+int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
+                  const void* v_new, uint32_t* err, oda_stream s) {
+  if (batch <= 0) return 0;
+  CommitParams c{};
+  c.L = p.L;
+  c.Hkv = p.Hkv;
+  c.D = p.D;
+  c.esize = p.esize;
+  c.sink = p.sink;
+  c.window = p.window;
+  c.ring_slots = p.ring_slots;
+  c.sw_window = p.sw_window;
+  c.block_shift = p.block_shift;
+  c.max_blocks = p.max_blocks;
+  c.batch = batch;           // k_new / v_new are [L][batch][Hkv][d]
+  c.ring_batch = p.max_batch;  // rings are [L?][max_batch][Hkv][slots][d]
+  c.num_blocks = kv.num_blocks;
+  c.n_layers_gated = p.Lg;
+  c.n_layers_sliding = p.Ls;
+  for (int l = 0; l < p.L; ++l) {
+    c.kind[l] = p.kind[l];
+    c.kidx[l] = p.kidx[l];
+  }
+  c.k_new = k_new;
+  c.v_new = v_new;
+  c.k_cache = kv.k_cache;
+  c.v_cache = kv.v_cache;
+  c.k_ring = kv.k_ring;
+  c.v_ring = kv.v_ring;
+  c.k_swring = kv.k_swring;
+  c.v_swring = kv.v_swring;
+  c.ring_pos = kv.ring_pos;
+  c.swring_pos = kv.swring_pos;
+  c.block_table = kv.block_table;
+  c.seq_len = kv.seq_len;
+  c.err = err;
+  hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(256), 0, s, c);
+  return (int)hipGetLastError();
+}
+
+int launch_prefill(const Plan& p, const oda_kv& kv, int32_t batch, int32_t layer,
+                   const void* k_src, const void* v_src, int64_t src_rows, uint32_t* err,
+                   oda_stream s) {
+  if (batch <= 0) return 0;
+  PrefillParams f{};
+  const bool gated = p.kind[layer] == ODA_LAYER_GATED;
+  f.Hkv = p.Hkv;
+  f.D = p.D;
+  f.esize = p.esize;
+  f.gated = gated;
+  f.sink = gated ? p.sink : 0;
+  f.window = gated ? p.window : p.sw_window;
+  f.slots = gated ? p.ring_slots : p.sw_window;
+  f.block_shift = p.block_shift;
+  f.max_blocks = p.max_blocks;
+  f.num_blocks = kv.num_blocks;
+  f.src_rows = src_rows;
+  f.rank = p.kidx[layer];
+  f.ring_batch = p.max_batch;
+  f.k_src = k_src;
+  f.v_src = v_src;
+  f.k_cache = kv.k_cache;
+  f.v_cache = kv.v_cache;
+  f.k_ring = gated ? kv.k_ring : kv.k_swring;
+  f.v_ring = gated ? kv.v_ring : kv.v_swring;
+  f.ring_pos = gated ? kv.ring_pos : kv.swring_pos;
+  f.block_table = kv.block_table;
+  f.seq_len = kv.seq_len;
+  f.err = err;
+  f.from_cache = 0;
+  const int64_t per_row = (int64_t)p.Hkv * p.D * p.esize / 16;
+  int64_t work = (src_rows > f.slots ? src_rows : f.slots) * per_row;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks, batch), dim3(256), 0, s, f);
+  return (int)hipGetLastError();
+}
+
+int launch_ring_init(const Plan& p, const oda_kv& kv, int32_t batch, uint32_t* err, oda_stream s) {
+  if (batch <= 0) return 0;
+  for (int l = 0; l < p.L; ++l) {
+    if (p.kind[l] != ODA_LAYER_GATED) continue;
+    PrefillParams f{};
+    f.Hkv = p.Hkv;
+    f.D = p.D;
+    f.esize = p.esize;
+    f.gated = 1;
+    f.sink = p.sink;
+    f.window = p.window;
+    f.slots = p.ring_slots;
+    f.block_shift = p.block_shift;
+    f.max_blocks = p.max_blocks;
+    f.num_blocks = kv.num_blocks;
+    f.src_rows = 0;
+    f.rank = p.kidx[l];
+    f.ring_batch = p.max_batch;
+    f.k_cache = kv.k_cache;
+    f.v_cache = kv.v_cache;
+    f.k_ring = kv.k_ring;
+    f.v_ring = kv.v_ring;
+    f.ring_pos = kv.ring_pos;
+    f.block_table = kv.block_table;
+    f.seq_len = kv.seq_len;
+    f.err = err;
+    f.from_cache = 1;
+    const int64_t work = (int64_t)p.ring_slots * p.Hkv * p.D * p.esize / 16;
+    const int64_t blocks = (work + 255) / 256;
+    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks, batch), dim3(256), 0, s, f);
+    const int rc = (int)hipGetLastError();
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int launch_access_set(const Plan& p, const oda_kv& kv, int32_t layer, int32_t b, int32_t mode,
+                      int32_t* positions, int64_t capacity, int64_t* count, uint32_t* err,
+                      oda_stream s) {
+  AccessParams a{};
+  const bool gated = p.kind[layer] == ODA_LAYER_GATED;
+  a.rows.source = (gated && mode == 1) ? kSrcPaged : kSrcRing;
+  a.rows.focus = p.focus;
+  a.rows.sink = gated ? p.sink : 0;
+  a.rows.window = gated ? p.window : p.sw_window;
+  a.rows.ring_slots = gated ? p.ring_slots : p.sw_window;
+  a.b = b;
+  a.block_shift = p.block_shift;
+  a.max_blocks = p.max_blocks;
+  a.seq_len = kv.seq_len;
+  a.focus_range = kv.focus_range;
+  a.positions = positions;
+  a.capacity = capacity;
+  a.count = count;
+  a.err = err;
+  hipLaunchKernelGGL(access_set_kernel, dim3(1), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_clear(void* ptr, size_t bytes, oda_stream s) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words <= 0) return 0;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(ptr), words);
+  return (int)hipGetLastError();
+}
+
+int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
+                 const int64_t* counter, int64_t num_steps, oda_stream s) {
+  StageParams sp{};
+  sp.n = n;
+  int64_t most = 0;
+  for (int i = 0; i < n; ++i) {
+    sp.src[i] = src[i];
+    sp.dst[i] = dst[i];
+    sp.bytes[i] = bytes[i];
+    if (bytes[i] > most) most = bytes[i];
+  }
+  sp.counter = counter;
+  sp.num_steps = num_steps;
+  int64_t blocks = (most / 16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL(stage_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+  return (int)hipGetLastError();
+}
+
+int launch_advance(int64_t* counter, oda_stream s) {
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, counter);
+  return (int)hipGetLastError();
+}
+
+}  // namespace oda

@@ -1,0 +1,229 @@
+/*
+ * oda.h -- C ABI of the On-Demand Attention (ODA) decode hot path on MI355X.
+ *
+ * The method (picx.dev summary of "On-Demand Attention: Language Models Know
+ * When to Recall", section "Local-First Decoding"): at decode position t every
+ * step first attends the Local access set
+ *     S^L_t = {1..min(s,t)} U {max(1,t-w+1)..t}      (s sinks, recent window w)
+ * then a recall score q_t decides, on the device, whether the same step is
+ * recomputed with Full attention over S^F_t = {1..t}: Full iff q_t > theta
+ * (theta = 0 by default); otherwise the Local result is accepted.  Section
+ * "Efficient Execution" of the same page names the runtime pieces rebuilt
+ * here: a persistent ring KV workspace serving Local, fused KV commits across
+ * layers, and GPU-side conditional execution of the Full pass.
+ *
+ * Conventions for every function below
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *     buffer and the stream; the library keeps no state between calls, never
+ *     allocates, never synchronises, and launches only kernels (no memset or
+ *     memcpy nodes), so every call may be recorded into a HIP graph.
+ *   - Element type of q, K and V is oda_dims.kv_dtype (bf16 or f32); outputs
+ *     and lse are always f32; accumulation is f32.
+ *   - seq_len[b] is the number of committed positions of request b.  During a
+ *     step the token being decoded is at position t = seq_len[b] + 1 and its
+ *     K/V come from the k_cur/v_cur (or k_new/v_new) arguments, not from the
+ *     caches.  seq_len[b] < 0 marks an inactive request slot: no kernel reads
+ *     or writes anything for it.
+ *   - Host-detectable argument errors return a negative status before any
+ *     launch.  Conditions only the device can see (a context beyond the block
+ *     table's capacity, a block id outside [0, num_blocks)) skip the affected
+ *     request and set a bit in the workspace error word (ODA_DEVERR_*).
+ *   - A workspace must not be shared by calls that may run concurrently.
+ */
+#ifndef ODA_H_
+#define ODA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as HIP's hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t* oda_stream;
+
+typedef enum {
+  ODA_OK = 0,
+  ODA_ERR_INVALID_ARG = -1,  /* a pointer, size or index is wrong            */
+  ODA_ERR_UNSUPPORTED = -2,  /* valid but not built (head_dim, group, dtype)  */
+  ODA_ERR_HIP = -3,          /* a kernel launch failed                        */
+  ODA_ERR_WORKSPACE = -4     /* workspace missing or smaller than required    */
+} oda_status;
+
+typedef enum { ODA_BF16 = 0, ODA_F32 = 1 } oda_dtype;
+
+/* Layer kinds.  GATED layers have distinct Local (sinks + window, served from
+ * the ring) and Full (whole paged cache) access sets.  SLIDING layers (hybrid
+ * backbones) read the same recent window in both modes, from their own ring,
+ * and keep no paged cache. */
+typedef enum { ODA_LAYER_GATED = 0, ODA_LAYER_SLIDING = 1 } oda_layer_kind;
+
+enum { ODA_MAX_LAYERS = 256, ODA_MAX_BATCH = 4096 };
+
+/* Bits of the device error word (first 4 bytes of the workspace). */
+enum { ODA_DEVERR_CAPACITY = 1, ODA_DEVERR_BLOCK_ID = 2, ODA_DEVERR_OUT_CAPACITY = 4 };
+
+/* Accounting counters, int64 per request (see oda_gate). */
+enum {
+  ODA_ACCT_STEPS = 0,        /* decode steps taken                           */
+  ODA_ACCT_FULL_CALLS,       /* steps whose gate fired                       */
+  ODA_ACCT_F_LOCAL,          /* sum of F_Local                               */
+  ODA_ACCT_F_FULL_TAKEN,     /* sum of a_t * F_Full(t)                       */
+  ODA_ACCT_F_FULL_ALWAYS,    /* sum of F_Full(t) (the always-Full cost)      */
+  ODA_ACCT_DELTA_F,          /* sum of (1-a_t) F_Full - F_Local - F_Recall   */
+  ODA_ACCT_KV_BYTES,         /* K/V bytes the taken passes attend            */
+  ODA_ACCT_F_RECALL,         /* sum of F_Recall                              */
+  ODA_ACCT_N
+};
+
+typedef struct {
+  int32_t num_layers;          /* L, 1..ODA_MAX_LAYERS                                   */
+  int32_t num_q_heads;         /* Hq                                                     */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0; query head h reads KV head h/(Hq/Hkv) */
+  int32_t head_dim;            /* d: 64 or 128                                           */
+  int32_t sink;                /* s >= 0 of gated layers                                 */
+  int32_t window;              /* w >= 1 of gated layers; gated ring has s+w slots       */
+  int32_t sw_window;           /* window of sliding layers (>= 1 when any exist)         */
+  int32_t block_size;          /* paged block in positions, a power of two (16)          */
+  int32_t max_batch;           /* request slots the caches and tables are sized for      */
+  int32_t max_blocks_per_seq;  /* columns of block_table                                 */
+  int32_t kv_dtype;            /* oda_dtype                                              */
+  int32_t focus;               /* 0: a fired gated layer reads S^F_t = {1..t};
+                                  1: it reads S^L_t U [a, b) (focus region per request)  */
+  int32_t full_splits;         /* split-K partitions per (request, KV head) of a Full
+                                  or focus pass; 0 = library default                     */
+  int32_t local_splits;        /* same for ring passes; 0 = default                      */
+  float   softmax_scale;       /* 0 -> 1/sqrt(head_dim)                                  */
+  int32_t reserved0;           /* must be 0                                              */
+  int64_t recall_flops;        /* F_Recall charged per request per step (accounting)     */
+  const uint8_t* layer_kind;   /* host [num_layers] of oda_layer_kind; NULL = all GATED  */
+} oda_dims;
+
+/* Let Lg / Ls be the numbers of gated / sliding layers.  A layer's cache index
+ * is its rank among the layers of its kind.  All arrays are dense, row-major. */
+typedef struct {
+  void* k_cache;               /* [Lg][num_blocks][Hkv][block_size][d]  paged history   */
+  void* v_cache;               /*   (position p of request b: block block_table[b][(p-1)/bs],
+                                     row (p-1) % bs)                                     */
+  void* k_ring;                /* [Lg][max_batch][Hkv][s+w][d]  Local ring workspace     */
+  void* v_ring;                /*   slot of position p: p-1 if p <= s, else s+(p-s-1) mod w */
+  void* k_swring;              /* [Ls][max_batch][Hkv][sw][d]   sliding-layer rings,     */
+  void* v_swring;              /*   slot (p-1) mod sw; NULL when Ls == 0                 */
+  int32_t* ring_pos;           /* [max_batch][s+w]  position held by each slot, 0 = none */
+  int32_t* swring_pos;         /* [max_batch][sw]   same for sliding rings (NULL if Ls == 0) */
+  const int32_t* block_table;  /* [max_batch][max_blocks_per_seq] physical block ids    */
+  int32_t* seq_len;            /* [max_batch] committed positions; < 0 = inactive slot   */
+  const int64_t* focus_range;  /* [max_batch][2] (a, b): 1-based, half-open; read only
+                                  when dims.focus != 0                                   */
+  int64_t num_blocks;          /* physical blocks per layer in k_cache / v_cache         */
+} oda_kv;
+
+/* Host.  Bytes of workspace any call below needs for `batch` requests (the
+ * first 256 bytes hold the device error word).  0 on invalid dims. */
+size_t oda_workspace_size(const oda_dims* dims, int32_t batch);
+
+/* Clears the workspace's error word and counters (a small kernel; call once
+ * after allocating a workspace).  The workspace needs no other initialisation. */
+oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspace,
+                              size_t workspace_bytes, oda_stream stream);
+
+/* After prefill: writes positions 1..seq_len[b] of layer `layer` from a dense
+ * source [batch][src_rows][Hkv][d] (row p-1 = position p) into the paged cache
+ * (gated layer) and into the layer's ring (the slots a one-by-one commit of
+ * those positions would leave), and sets ring_pos / swring_pos.  Needs
+ * seq_len[b] <= src_rows. */
+oda_status oda_prefill_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch, int32_t layer,
+                          const void* k_src, const void* v_src, int64_t src_rows,
+                          void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* Rebuilds every gated layer's ring (and ring_pos) from the paged cache for
+ * the committed positions 1..seq_len[b]. */
+oda_status oda_ring_init(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                         void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* The fused cross-layer KV commit ("Efficient Execution"): one launch writes
+ * the token at position t = seq_len[b]+1 of every layer -- k_new/v_new
+ * [L][batch][Hkv][d] -- into the paged cache (gated layers) and the ring slot
+ * of t (all layers), records t in ring_pos / swring_pos, then sets
+ * seq_len[b] = t. */
+oda_status oda_commit_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                         const void* k_new, const void* v_new,
+                         void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* The Local pass of one layer for every active request: softmax attention of
+ * q [batch][Hq][d] over S^L_t (gated layer: sinks + window, from the ring;
+ * sliding layer: its window) where position t is k_cur/v_cur [batch][Hkv][d].
+ * Writes out [batch][Hq][d] and lse [batch][Hq] (natural log; nullable). */
+oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
+                            const void* q, const void* k_cur, const void* v_cur,
+                            float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* The gate plus the Full pass of one layer.  A request fires iff
+ * recall_score[b] > theta (strict; NaN never fires; inactive slots never
+ * fire).  Fired requests, compacted in ascending order, attend S^F_t
+ * (or S^L_t U [a,b) when dims.focus; sliding layers: their window) over the
+ * paged cache with position t from k_cur/v_cur, and their rows of out / lse
+ * are overwritten; rows of requests that did not fire are left as they are
+ * (the accepted Local result).  call_list [batch] (ascending request ids,
+ * then -1) and call_count [1] are written when not NULL. */
+oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t layer,
+                                 int32_t batch, const void* q, const void* k_cur,
+                                 const void* v_cur, const float* recall_score, float theta,
+                                 float* out, float* lse, int32_t* call_list, int32_t* call_count,
+                                 void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* The gate on its own, with the per-step accounting of the "Computational
+ * Savings" section (dF = (1-a) F_Full - F_Local - F_Recall, F = 4*Hq*d per
+ * attended position per layer).  Writes call_list / call_count (nullable);
+ * adds the decisions to full_calls [batch] and the step's figures to
+ * counters [batch][ODA_ACCT_N] (both nullable). */
+oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                    const float* recall_score, float theta, int32_t* call_list,
+                    int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                    oda_stream stream);
+
+/* One whole decode step for every active request, in this order: the Local
+ * pass of every layer, the gate (with accounting), the Full pass of every
+ * layer for the fired requests, then the fused commit.  q_local / q_full
+ * [L][batch][Hq][d] (q_full NULL: reuse q_local), k_new / v_new
+ * [L][batch][Hkv][d], out [L][batch][Hq][d] (the accepted result), lse
+ * [L][batch][Hq] (nullable).  Capture it once into a HIP graph and replay it
+ * to run the step without any host round trip. */
+oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                    const void* q_local, const void* q_full, const void* k_new,
+                    const void* v_new, const float* recall_score, float theta,
+                    float* out, float* lse, int32_t* call_list, int32_t* call_count,
+                    int64_t* full_calls, int64_t* counters,
+                    void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* The positions layer `layer` would attend for request b in the given mode
+ * (0 Local, 1 Full) at t = seq_len[b]+1, derived by the same device index
+ * code the attention kernels use: *count is set to the set size and the
+ * members are written, in no particular order, to positions [capacity].
+ * Sets ODA_DEVERR_OUT_CAPACITY if capacity is too small. */
+oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t b,
+                          int32_t mode, int32_t* positions, int64_t capacity, int64_t* count,
+                          void* workspace, size_t workspace_bytes, oda_stream stream);
+
+/* Input staging for replayed graphs: for i < n copies bytes[i] bytes from
+ * src[i] + k*bytes[i] to dst[i], where k = *step_counter mod num_steps.
+ * src, dst and bytes are HOST arrays of n <= 8 entries (their values are
+ * baked into the launch); the buffers they point to are device memory and
+ * every bytes[i] must be a multiple of 16. */
+oda_status oda_stage_step(int32_t n, const void* const* src, void* const* dst,
+                          const int64_t* bytes, const int64_t* step_counter, int64_t num_steps,
+                          oda_stream stream);
+
+/* *step_counter += 1 (one tiny kernel; the last node of a replayed step). */
+oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream);
+
+/* Host.  Human-readable status name. */
+const char* oda_status_string(oda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ODA_H_ */

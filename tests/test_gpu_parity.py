@@ -1,0 +1,272 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Integer results -- gate decisions, compacted call lists, counts, Full-call
+totals, accounting counters, access sets, ring slot contents -- must match
+bit for bit; attention outputs within the bars of tests/gpu_helpers.TOL.
+Inputs are seeded synthetic draws; sizes span several tiles, ragged tails,
+ring wrap-around, the t <= s+w regime and empty prefixes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from gated_kv_access_amd import binding as B
+from gated_kv_access_amd import workloads as W
+from gated_kv_access_amd.state import DecodeState
+from tests.gpu_helpers import (assert_outputs_close, oracle_cfg, oracle_sequences, run_steps, say,
+                               words, LSE_TOL)
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(name, **kw):
+    base = dict(num_layers=2, num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16", batch=3,
+                prefill=(0, 700, 3001), steps=10, sink=4, window=256, score_mode="normal", seed=101)
+    base.update(kw)
+    return W.Workload(name, **base)
+
+
+SMALL = [
+    _small("bf16_d128_g2"),
+    _small("bf16_d64_g1", head_dim=64, num_q_heads=2, num_kv_heads=2, seed=102),
+    _small("bf16_d128_g4", num_q_heads=8, num_kv_heads=2, seed=103),
+    _small("f32_d128_g2", dtype="f32", seed=104),
+    _small("f32_d64_g4_bs8", dtype="f32", head_dim=64, num_q_heads=4, num_kv_heads=1, block_size=8, seed=105),
+    _small("bf16_ring_wrap_bs64", sink=2, window=16, prefill=(100, 37, 5), steps=40, block_size=64, seed=106),
+    _small("bf16_no_sinks", sink=0, window=33, prefill=(64, 1, 200), steps=12, seed=107),
+]
+
+
+def _check_run(wl, graph=False, q_full=False):
+    say(f"{wl.name}: prefill {wl.prefill}, {wl.steps} steps, graph={graph}")
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")
+    qf = W.gen_queries(wl, "cpu", tag=4) if q_full else None
+    scores = W.gen_scores(wl)
+    got = run_steps(st, q, scores, graph=graph, q_full=qf)
+    assert st.device_error() == 0
+    ks, vs = oracle_sequences(st)
+    want = orc.decode_run(oracle_cfg(wl), wl.prefill, ks, vs, words(q), scores,
+                          q_full=None if qf is None else words(qf),
+                          focus=st.focus_range.cpu().numpy() if wl.focus else None)
+    # integer results: bit-exact
+    assert np.array_equal(got.call_count, want["call_count"])
+    assert np.array_equal(got.call_list, want["call_list"])
+    assert np.array_equal(got.full_calls, want["full_calls"])
+    assert np.array_equal(got.counters, want["acct"])
+    assert_outputs_close(got.out, want["out"], wl.dtype, wl.name)
+    lse_err = float(np.abs(got.lse - want["lse"]).max())
+    assert lse_err <= LSE_TOL[wl.dtype], lse_err
+    return st, got, want
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_runs_match_oracle(wl):
+    _check_run(wl)
+
+
+def test_tiny_config_every_step():
+    """The 1-layer fp32 workload (300-token prefill, 50 steps, s=4, w=64) step by step."""
+    _check_run(W.config(0))
+
+
+def test_graph_replay_matches_oracle_and_eager():
+    wl = _small("graph_bf16", prefill=(50, 900, 2100), steps=16, seed=111)
+    _, g_run, _ = _check_run(wl, graph=True)
+    _, e_run, _ = _check_run(wl, graph=False)
+    assert np.array_equal(g_run.out, e_run.out), "graph replay differs from eager launches"
+    assert np.array_equal(g_run.counters, e_run.counters)
+
+
+def test_separate_full_pass_queries():
+    _check_run(_small("q_full_bf16", prefill=(10, 400, 1500), steps=8, seed=112), q_full=True)
+
+
+def test_local_equals_full_while_t_within_s_plus_w():
+    """t <= s+w: S^L_t = S^F_t, so the ring pass and the paged pass agree."""
+    wl = _small("short_ctx", prefill=(0, 20, 200), steps=8, window=256, seed=113)
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")
+    never = np.full((wl.steps, wl.batch), -1.0, np.float32)
+    always = np.full((wl.steps, wl.batch), 1.0, np.float32)
+    r_local = run_steps(st, q, never)
+    st2 = DecodeState(wl, gen_device="cpu")
+    st2.prefill()
+    r_full = run_steps(st2, q, always)
+    diff = np.abs(r_local.out - r_full.out).max()
+    say(f"ring vs paged max diff {diff:.3e}")
+    assert diff <= 1e-5
+    assert r_full.full_calls.tolist() == [wl.steps] * wl.batch
+
+
+HYBRID = [
+    _small("hybrid_full", num_layers=8, sw_window=64, sink=4, window=128, batch=2, prefill=(1000, 2500),
+           steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)), seed=121),
+    _small("hybrid_focus", num_layers=8, sw_window=64, sink=4, window=128, batch=3,
+           prefill=(1000, 2500, 6000), steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)),
+           focus=True, seed=122),
+    _small("focus_only_gated", num_layers=2, batch=3, prefill=(5000, 300, 4300), steps=6, focus=True, seed=123),
+]
+
+
+@pytest.mark.parametrize("wl", HYBRID, ids=[w.name for w in HYBRID])
+def test_hybrid_and_focus_runs_match_oracle(wl):
+    _check_run(wl)
+
+
+def test_focus_region_overlapping_window_and_sinks():
+    wl = _small("focus_overlap", num_layers=1, batch=3, prefill=(4500, 4500, 4500), steps=4, focus=True,
+                sink=4, window=256, seed=124)
+    st = DecodeState(wl, gen_device="cpu")
+    # regions: overlapping the window, covering the sinks, straddling nothing
+    st.focus_range.copy_(torch.tensor([[4300, 4400 + 4096], [1, 4097], [2000, 2000 + 4096]], dtype=torch.int64))
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")
+    scores = np.ones((wl.steps, wl.batch), np.float32)
+    got = run_steps(st, q, scores)
+    ks, vs = oracle_sequences(st)
+    want = orc.decode_run(oracle_cfg(wl), wl.prefill, ks, vs, words(q), scores,
+                          focus=st.focus_range.cpu().numpy())
+    assert np.array_equal(got.counters, want["acct"])
+    assert_outputs_close(got.out, want["out"], wl.dtype, wl.name)
+
+
+# ---------------------------------------------------------------- integer exports
+
+def _ring_slot(p, s, w):
+    return p - 1 if p <= s else s + (p - s - 1) % w
+
+
+@pytest.mark.parametrize("wl", [SMALL[5], SMALL[6], HYBRID[1]], ids=["wrap", "nosink", "hybrid"])
+def test_access_sets_and_ring_slots_bit_exact(wl):
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")
+    scores = W.gen_scores(wl)
+    k_new, v_new = st.decode_inputs()
+    cfg = oracle_cfg(wl)
+    pos = torch.zeros(wl.max_rows + 8, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    from gated_kv_access_amd.runner import StepRunner
+    r = StepRunner(st, q.cuda(), k_new, v_new, torch.from_numpy(scores).cuda())
+    for k in range(wl.steps + 1):
+        for b in range(wl.batch):
+            t = wl.prefill[b] + k + 1
+            fa, fb = (int(x) for x in st.focus_range[b].tolist())
+            for layer in range(wl.num_layers):
+                kind = wl.kinds[layer]
+                for mode in (0, 1):
+                    B.access_set(st.dims, st.kv, layer, b, mode, pos, cnt, st.workspace)
+                    torch.cuda.synchronize()
+                    n = int(cnt[0].item())
+                    got = np.sort(pos[:n].cpu().numpy().astype(np.int64))
+                    want = orc.access_set(cfg, kind, mode, t, fa, fb)
+                    assert np.array_equal(got, want), (wl.name, k, b, layer, mode, t)
+            # ring slot contents: what one-by-one commits of 1..t-1 leave
+            if wl.gated_layers:
+                s, w = wl.sink, wl.window
+                ring = np.zeros(s + w, np.int64)
+                for p in range(1, t):
+                    ring[_ring_slot(p, s, w)] = p
+                assert np.array_equal(st.ring_pos[b].cpu().numpy(), ring), (k, b)
+            if wl.sliding_layers:
+                ring = np.zeros(wl.sw_window, np.int64)
+                for p in range(1, t):
+                    ring[(p - 1) % wl.sw_window] = p
+                assert np.array_equal(st.swring_pos[b].cpu().numpy(), ring), (k, b)
+        if k < wl.steps:
+            r.step_eager()
+    assert st.device_error() == 0
+
+
+def test_commit_writes_paged_cache_and_ring_bit_exact():
+    wl = _small("commit", prefill=(3, 31, 70), steps=20, sink=2, window=8, block_size=16, seed=131)
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")
+    run_steps(st, q, W.gen_scores(wl))
+    bt = st.block_table.cpu().numpy()
+    for layer in range(wl.num_layers):
+        for b in range(wl.batch):
+            k_all = st.sequence(layer, b, "k")
+            v_all = st.sequence(layer, b, "v")
+            t_end = wl.prefill[b] + wl.steps
+            for p in range(1, t_end + 1):
+                blk = bt[b, (p - 1) // wl.block_size]
+                row = (p - 1) % wl.block_size
+                assert torch.equal(st.k_cache[layer, blk, :, row], k_all[p - 1])
+                assert torch.equal(st.v_cache[layer, blk, :, row], v_all[p - 1])
+            for j in range(wl.sink + wl.window):
+                p = int(st.ring_pos[b, j].item())
+                if p:
+                    assert torch.equal(st.k_ring[layer, b, :, j], k_all[p - 1])
+                    assert torch.equal(st.v_ring[layer, b, :, j], v_all[p - 1])
+    assert st.seq_len.cpu().tolist() == [p + wl.steps for p in wl.prefill]
+
+
+def test_gate_and_accounting_bit_exact():
+    wl = _small("gate", batch=1100, prefill=tuple([100] * 1100), num_layers=3, steps=1, seed=141)
+    dims = __import__("gated_kv_access_amd.state", fromlist=["make_dims"]).make_dims(wl, recall_flops=1234)
+    seq = torch.tensor(list(range(0, 2200, 2)), dtype=torch.int32, device="cuda")
+    seq[7] = -1   # inactive slot
+    kv = B.OdaKV()
+    kv.seq_len = seq.data_ptr()
+    rng = np.random.default_rng(5)
+    score = rng.standard_normal(1100).astype(np.float32)
+    score[[3, 64, 65, 1023, 1024]] = [0.0, -0.0, np.nan, np.inf, 1e-45]
+    sc = torch.from_numpy(score).cuda()
+    call_list = torch.full((1100,), 77, dtype=torch.int32, device="cuda")
+    call_count = torch.zeros(4, dtype=torch.int32, device="cuda")
+    full_calls = torch.zeros(1100, dtype=torch.int64, device="cuda")
+    counters = torch.zeros((1100, 8), dtype=torch.int64, device="cuda")
+    B.gate(dims, kv, 1100, sc, 0.0, call_list, call_count, full_calls, counters)
+    torch.cuda.synchronize()
+    seq_h = seq.cpu().numpy()
+    fired = np.array([seq_h[b] >= 0 and orc.gate(float(score[b]), 0.0) for b in range(1100)])
+    want_list = np.flatnonzero(fired)
+    got_count = int(call_count[0].item())
+    assert got_count == want_list.size
+    assert np.array_equal(call_list[:got_count].cpu().numpy(), want_list)
+    assert np.all(call_list[got_count:].cpu().numpy() == -1)
+    assert np.array_equal(full_calls.cpu().numpy(), fired.astype(np.int64))
+    cfg = oracle_cfg(wl, recall_flops=1234)
+    got_c = counters.cpu().numpy()
+    for b in range(1100):
+        if seq_h[b] < 0:
+            assert np.all(got_c[b] == 0)
+            continue
+        want = orc.step_accounting(cfg, int(seq_h[b]) + 1, bool(fired[b]))
+        assert got_c[b].tolist() == [want[f] for f in orc.ACCT_FIELDS], b
+
+
+# ---------------------------------------------------------------- standalone per-layer calls
+
+def test_standalone_local_and_gated_full_calls():
+    wl = _small("standalone", prefill=(0, 1200, 2600), steps=1, seed=151)
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")[0].cuda()          # [L][B][Hq][d]
+    k_new, v_new = st.decode_inputs()
+    score = torch.tensor([0.5, -0.25, 2.0], dtype=torch.float32, device="cuda")
+    ks, vs = oracle_sequences(st)
+    want = orc.decode_run(oracle_cfg(wl), wl.prefill, ks, vs, words(q.unsqueeze(0)),
+                          score.cpu().numpy()[None, :])
+    for layer in range(wl.num_layers):
+        out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), 5.0, device="cuda")
+        lse = torch.zeros((wl.batch, wl.num_q_heads), device="cuda")
+        B.decode_local(st.dims, st.kv, layer, wl.batch, q[layer].contiguous(), k_new[0, layer].contiguous(),
+                       v_new[0, layer].contiguous(), out, lse, st.workspace)
+        local = out.clone()
+        call_list = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+        call_count = torch.zeros(4, dtype=torch.int32, device="cuda")
+        B.decode_full_gated(st.dims, st.kv, layer, wl.batch, q[layer].contiguous(), k_new[0, layer].contiguous(),
+                            v_new[0, layer].contiguous(), score, 0.0, out, lse, call_list, call_count,
+                            st.workspace)
+        torch.cuda.synchronize()
+        assert call_list.cpu().tolist() == [0, 2, -1] and int(call_count[0]) == 2
+        assert torch.equal(out[1], local[1]), "a request that did not fire keeps its Local row"
+        assert_outputs_close(out.cpu().numpy()[None, None], want["out"][:, layer:layer + 1], wl.dtype,
+                             f"standalone layer {layer}")
