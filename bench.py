@@ -1,0 +1,286 @@
+"""Decode-step throughput of the ODA hot path on one MI355X.
+
+Workload (default): 28 layers, 16 query / 8 KV heads of 128, bf16 K/V,
+batch 1, 131072-token prefilled context, s = 4, w = 2048, paged blocks of 16,
+recall scores drawn so exactly 12.5% of the timed steps fire.  One step is
+the whole hot path -- Local pass of every layer, device gate, gated Full pass
+of every layer, fused commit -- replayed from a captured HIP graph.
+
+Prints one JSON line: steps/s (value), effective KV GB/s and its share of
+HBM peak, the roofline of the dominant kernel (the Full-pass attention kernel,
+timed with HIP events on its launch stream), and the CPU oracle timed on a
+bounded sample as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_attention_ctx128k.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_kv_access_amd", "csrc", "oda_kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--rho", type=float, default=None, help="override the Full-call rate")
+    ap.add_argument("--roofline-launches", type=int, default=56)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time rho=0, rho=1 and always-Full for the savings check")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from gated_kv_access_amd import binding as B
+    from gated_kv_access_amd import workloads as W
+    from gated_kv_access_amd.runner import StepRunner
+    from gated_kv_access_amd.state import DecodeState
+
+    B.load()
+    K, Wm = args.steps, args.warmup
+    base = W.config(2)
+    rho = base.rho[0] if args.rho is None else args.rho
+    wl = base.with_(steps=Wm + K, rho=(rho,))
+    log(f"workload {wl.name}: prefill {wl.prefill[0]}, warmup {Wm}, timed {K}, rho {rho}")
+    t0 = time.time()
+    st = DecodeState(wl, gen_device="cuda")
+    st.prefill()
+    q = W.gen_queries(wl, "cuda")
+    k_new, v_new = st.decode_inputs()
+    sc = np.concatenate([W.gen_scores(wl.with_(steps=Wm)), W.gen_scores(wl.with_(steps=K))], 0) \
+        if Wm > 0 else W.gen_scores(wl.with_(steps=K))
+    scores = torch.from_numpy(sc).cuda()
+    log(f"setup {time.time() - t0:.1f}s (prefill of {wl.num_layers} layers x {wl.prefill[0]} positions)")
+
+    r = StepRunner(st, q, k_new, v_new, scores, want_lse=False)
+    r.capture()
+    r.replay(Wm)
+    torch.cuda.synchronize()
+    acct0 = r.counters.clone()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    r.replay(K)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    if st.device_error() != 0:
+        log(f"device error word {st.device_error()}")
+        return 1
+    acct = (r.counters - acct0).cpu().numpy()[0]
+    f = dict(zip(B.ACCT_FIELDS, acct.tolist()))
+    steps_per_s = K / (ms / 1e3)
+    kv_gbps = f["kv_bytes"] / (ms / 1e3) / 1e9
+    log(f"timed {K} steps in {ms:.1f} ms: {steps_per_s:.1f} steps/s, {kv_gbps:.0f} GB/s effective KV, "
+        f"{f['full_calls']} Full calls")
+
+    # ---------------------------------------------------------------- roofline leg
+    # The dominant kernel: the Full-pass attention kernel (split-K over the paged
+    # cache + last-workgroup merge), one launch per oda_decode_full_gated call,
+    # every call firing.  Timed over all its launches with HIP events on the stream
+    # the launches go to (torch's current stream).
+    L, Hkv, d = wl.num_layers, wl.num_kv_heads, wl.head_dim
+    t_now = int(st.seq_len[0].item()) + 1
+    fire = torch.ones(4, dtype=torch.float32, device="cuda")
+    out = torch.empty((1, wl.num_q_heads, d), dtype=torch.float32, device="cuda")
+    qs = [q[-1, l].contiguous() for l in range(L)]
+    ks = [k_new[-1, l].contiguous() for l in range(L)]
+    vs = [v_new[-1, l].contiguous() for l in range(L)]
+    R = args.roofline_launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(R):
+        l = i % L
+        B.decode_full_gated(st.dims, st.kv, l, 1, qs[l], ks[l], vs[l], fire, 0.0, out, None, None, None,
+                            st.workspace)
+    e1.record()
+    torch.cuda.synchronize()
+    avg_us = e0.elapsed_time(e1) * 1e3 / R
+    bytes_per_launch = (t_now - 1) * Hkv * d * 2 * wl.esize  # K and V rows streamed from the paged cache
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_sha") == kernel_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "attention_kernel<bf16,128,G2,paged,ballot>", "avg_launch_us": round(avg_us, 2),
+                "bytes_per_launch": bytes_per_launch, "launches": R}
+    log(f"roofline: Full-pass kernel {avg_us:.1f} us/launch, {achieved:.0f} GB/s = "
+        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak")
+
+    extra = {}
+    if args.sweep:
+        extra = sweep(st, wl, q, k_new, v_new, K, Wm, log)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(st, wl, q, rho, args.cpu_layers, log)
+
+    res = {
+        "metric": "decode steps/s and effective KV GB/s (% HBM peak) at 128K ctx, rho=0.125",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "q_heads": wl.num_q_heads, "kv_heads": Hkv,
+                   "head_dim": d, "batch": wl.batch, "prefill": wl.prefill[0], "sink": wl.sink,
+                   "window": wl.window, "block_size": wl.block_size, "rho": rho,
+                   "full_calls_timed": int(f["full_calls"]), "parallelism": "single GPU"},
+        "tokens_per_s": round(steps_per_s * wl.batch, 2),
+        "effective_kv_gbps": round(kv_gbps, 1),
+        "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "flops_ratio_vs_full": round((f["f_local"] + f["f_full_taken"] + f["f_recall"]) / f["f_full_always"], 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def sweep(st, wl, q, k_new, v_new, K, Wm, log):
+    """rho = 0, rho = 1 and always-Full over the same K steps, for the step-time
+    ratio against the FLOP prediction of the per-step savings equation."""
+    import numpy as np
+    import torch
+
+    from gated_kv_access_amd import binding as B
+    from gated_kv_access_amd.runner import StepRunner
+
+    P = wl.prefill[0]
+    out = {}
+
+    def time_runner(r, label):
+        st.seq_len.fill_(P + Wm)
+        B.ring_init(st.dims, st.kv, 1, st.workspace)  # ring state of the reset context
+        r.capture()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        r.replay(K)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1)
+        log(f"sweep {label}: {K / (ms / 1e3):.1f} steps/s ({ms / K * 1e3:.1f} us/step)")
+        return ms / K
+
+    for label, val in (("rho0", -1.0), ("rho1", 1.0)):
+        sc = torch.full((Wm + K, 1), val, dtype=torch.float32, device="cuda")
+        r = StepRunner(st, q, k_new, v_new, sc, want_lse=False)
+        r.step_counter[0] = Wm
+        out[f"us_per_step_{label}"] = round(time_runner(r, label) * 1e3, 2)
+    # Always-Full: every layer's Full pass and the commit, no Local attempt, no gate.
+    fire = torch.ones(4, dtype=torch.float32, device="cuda")
+    L = wl.num_layers
+    o = torch.empty((L, 1, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    ctr = torch.tensor([Wm, 0], dtype=torch.int64, device="cuda")
+    qb, kb, vb = torch.empty_like(q[0]), torch.empty_like(k_new[0]), torch.empty_like(v_new[0])
+
+    class FullOnly:
+        def capture(self):
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    B.stage_step([q, k_new, v_new], [qb, kb, vb], ctr, q.shape[0])
+                    for l in range(L):
+                        B.decode_full_gated(st.dims, st.kv, l, 1, qb[l], kb[l], vb[l], fire, 0.0, o[l], None,
+                                            None, None, st.workspace)
+                    B.commit_kv(st.dims, st.kv, 1, kb, vb, st.workspace)
+            torch.cuda.current_stream().wait_stream(s)
+            self.g = g
+
+        def replay(self, n):
+            for _ in range(n):
+                self.g.replay()
+
+    ms_full = time_runner(FullOnly(), "always-Full")
+    out["us_per_step_full_only"] = round(ms_full * 1e3, 2)
+    st.seq_len.fill_(P + Wm + K)
+    return {"sweep": out}
+
+
+def cpu_baseline(st, wl, q, rho, n_layers, log):
+    """The fp64 oracle on the host cores over a bounded sample: n_layers of the 28
+    layers, 2 Local-only and 2 fired steps at the end of the timed context,
+    scaled linearly to all layers and combined as T(rho) = (1-rho) T_L + rho T_F."""
+    import numpy as np
+    import torch
+
+    import oracle as orc
+    from gated_kv_access_amd import workloads as W
+
+    t_end = int(st.seq_len[0].item())  # positions committed by the end of the run
+    k = 2
+    P0 = t_end - k
+    layers = list(range(n_layers))
+    rows = t_end
+    ks = np.zeros((n_layers, 1, rows, wl.num_kv_heads, wl.head_dim), np.uint16)
+    vs = np.zeros_like(ks)
+    for i, l in enumerate(layers):
+        ks[i, 0] = W.gen_sequence(wl, l, 0, "k", "cuda")[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        vs[i, 0] = W.gen_sequence(wl, l, 0, "v", "cuda")[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    qq = q[:k, :n_layers].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    cfg = orc.OracleConfig(n_layers, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, sink=wl.sink,
+                           window=wl.window, dtype=orc.BF16)
+    threads = orc.get_threads()
+    times = {}
+    for label, val in (("local", -1.0), ("full", 1.0)):
+        sc = np.full((k, 1), val, np.float32)
+        t0 = time.perf_counter()
+        orc.decode_run(cfg, [P0], ks, vs, qq, sc)
+        times[label] = (time.perf_counter() - t0) / k * (wl.num_layers / n_layers)
+    t_step = (1 - rho) * times["local"] + rho * times["full"]
+    log(f"cpu oracle ({threads} threads): Local step {times['local']:.3f}s, Full step {times['full']:.3f}s "
+        f"(scaled to {wl.num_layers} layers)")
+    return {"value": round(1.0 / t_step, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_layers} of {wl.num_layers} layers, {k} Local-only + {k} fired steps at "
+                      f"t={P0 + 1}..{t_end}, scaled linearly to all layers, "
+                      f"T(rho)=(1-rho)T_L+rho*T_F with rho={rho}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,7 +18,9 @@ using oda::WsLayout;
 
 namespace {
 
-constexpr int32_t kDefaultFullGroups = 1024;  // workgroups a Full pass aims for
+constexpr int32_t kComputeUnits = 256;        // MI355X: one 8-wave workgroup fills a CU
+constexpr int32_t kFullRowsPerSplit = 16384;  // beyond this, more rounds of workgroups
+constexpr int32_t kMaxSplits = 512;           // merge weights are staged in LDS
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
@@ -86,18 +88,30 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
   if (p->Lg > 0) {
     const int64_t max_ctx = (int64_t)p->max_blocks * p->block_size;
     const int32_t tiles = ceil_div(max_ctx, tile);
-    int32_t f = d->full_splits > 0 ? d->full_splits : ceil_div(kDefaultFullGroups, (int64_t)b * p->Hkv);
+    int32_t f = d->full_splits;
+    if (f <= 0) {
+      // Whole rounds of kComputeUnits workgroups: `round` splits per (request,
+      // KV head) fill the chip once; long contexts take several rounds so that
+      // requests of different lengths balance through dynamic dispatch.
+      const int64_t pairs = (int64_t)b * p->Hkv;
+      const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)(kComputeUnits / pairs);
+      f = ceil_div(max_ctx, kFullRowsPerSplit);
+      f = ceil_div(f, round) * round;
+    }
     if (f > tiles) f = tiles;
+    if (f > kMaxSplits) f = kMaxSplits;
     p->full_splits = f < 1 ? 1 : f;
     const int32_t rtiles = ceil_div(p->ring_slots, tile);
-    int32_t l = d->local_splits > 0 ? d->local_splits : rtiles;
+    int32_t l = d->local_splits > 0 ? d->local_splits : rtiles;  // one tile per workgroup
     if (l > rtiles) l = rtiles;
+    if (l > kMaxSplits) l = kMaxSplits;
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
     const int32_t stiles = ceil_div(p->sw_window, tile);
     int32_t s = d->local_splits > 0 ? d->local_splits : stiles;
     if (s > stiles) s = stiles;
+    if (s > kMaxSplits) s = kMaxSplits;
     p->sw_splits = s < 1 ? 1 : s;
   }
 }
@@ -113,7 +127,9 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.err_off = 0;
   w.count_off = 4;
   w.list_off = oda::kWsHeader;
-  w.part_o_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.ticket_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.commit_ticket_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
+  w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
   w.total = up(w.part_ml_off + sizeof(float) * 2 * (size_t)b * p.Hq * ms);
   return w;
@@ -162,24 +178,30 @@ oda_status check_kv(const Plan& p, const oda_kv* kv, bool need_gated_cache, bool
 
 oda_status hip_status(int rc) { return rc == 0 ? ODA_OK : ODA_ERR_HIP; }
 
-// Attention pass of one layer: `full` selects the gated Full pass.
-oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, bool full,
+// Attention pass of one layer.  gate: kGateAll (Local pass of every active
+// request), kGateList (Full pass of the step's compacted list) or kGateBallot
+// (Full pass that compacts score > theta itself).
+oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, int32_t gate,
                     const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
-                    const int32_t* call_list, const int32_t* call_count, oda_stream s) {
+                    const int32_t* call_list, const int32_t* call_count, const float* score,
+                    float theta, int32_t* list_out, int32_t* count_out, oda_stream s) {
   const Plan& p = c.plan;
   const bool gated = p.kind[layer] == ODA_LAYER_GATED;
+  const bool full = gate != oda::kGateAll;
   oda::AttnParams a{};
   a.rows.source = (gated && full) ? oda::kSrcPaged : oda::kSrcRing;
   a.rows.focus = p.focus;
   a.rows.sink = gated ? p.sink : 0;
   a.rows.window = gated ? p.window : p.sw_window;
   a.rows.ring_slots = gated ? p.ring_slots : p.sw_window;
+  a.gate_mode = gate;
+  a.batch = batch;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.splits = a.rows.source == oda::kSrcPaged ? p.full_splits : (gated ? p.local_splits : p.sw_splits);
-  a.tile_rows = p.tile_rows;
   a.max_blocks = p.max_blocks;
   a.block_shift = p.block_shift;
+  a.capacity = p.max_blocks * p.block_size;
   a.num_blocks = kv->num_blocks;
   const int64_t row_bytes = (int64_t)p.D * p.esize;
   const int64_t rank = p.kidx[layer];
@@ -195,36 +217,23 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.block_table = kv->block_table;
   a.seq_len = kv->seq_len;
   a.focus_range = kv->focus_range;
-  a.call_list = full ? call_list : nullptr;
-  a.call_count = full ? call_count : nullptr;
+  a.call_list = call_list;
+  a.call_count = call_count;
+  a.score = score;
+  a.theta = theta;
+  a.call_list_out = list_out;
+  a.call_count_out = count_out;
   a.q = q;
+  a.k_cur = k_cur;
+  a.v_cur = v_cur;
+  a.out = out;
+  a.lse = lse;
   a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
+  a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
-  a.capacity = p.max_blocks * p.block_size;
-  int rc = oda::launch_attention(p, a, batch, s);
-  if (rc) return ODA_ERR_HIP;
-  oda::MergeParams m{};
-  m.rows = a.rows;
-  m.Hq = p.Hq;
-  m.Hkv = p.Hkv;
-  m.splits = a.splits;
-  m.tile_rows = p.tile_rows;
-  m.capacity = a.capacity;
-  m.seq_len = kv->seq_len;
-  m.focus_range = kv->focus_range;
-  m.call_list = a.call_list;
-  m.call_count = a.call_count;
-  m.q = q;
-  m.k_cur = k_cur;
-  m.v_cur = v_cur;
-  m.part_o = a.part_o;
-  m.part_ml = a.part_ml;
-  m.out = out;
-  m.lse = lse;
-  m.scale_log2 = p.scale_log2;
-  return hip_status(oda::launch_merge(p, m, batch, s));
+  return hip_status(oda::launch_attention(p, a, batch, s));
 }
 
 }  // namespace
@@ -277,7 +286,8 @@ oda_status oda_commit_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch, 
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return ODA_ERR_INVALID_ARG;
   st = check_kv(c.plan, kv, true, true);
   if (st != ODA_OK) return st;
-  return hip_status(oda::launch_commit(c.plan, *kv, batch, k_new, v_new, c.err, stream));
+  return hip_status(oda::launch_commit(c.plan, *kv, batch, k_new, v_new,
+                                       reinterpret_cast<int32_t*>(c.base + c.ws.commit_ticket_off), c.err, stream));
 }
 
 oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
@@ -290,7 +300,8 @@ oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t laye
   if (!aligned16(q)) return ODA_ERR_INVALID_ARG;
   st = check_kv(c.plan, kv, false, true);
   if (st != ODA_OK) return st;
-  return run_pass(c, kv, layer, batch, false, q, k_cur, v_cur, out, lse, nullptr, nullptr, stream);
+  return run_pass(c, kv, layer, batch, oda::kGateAll, q, k_cur, v_cur, out, lse, nullptr, nullptr, nullptr,
+                  0.f, nullptr, nullptr, stream);
 }
 
 oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
@@ -307,11 +318,8 @@ oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t
   const bool gated = c.plan.kind[layer] == ODA_LAYER_GATED;
   st = check_kv(c.plan, kv, gated, !gated);
   if (st != ODA_OK) return st;
-  int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
-  int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
-  int rc = oda::launch_gate(c.plan, *kv, batch, recall_score, theta, list, count, nullptr, nullptr, stream);
-  if (rc) return ODA_ERR_HIP;
-  return run_pass(c, kv, layer, batch, true, q, k_cur, v_cur, out, lse, list, count, stream);
+  return run_pass(c, kv, layer, batch, oda::kGateBallot, q, k_cur, v_cur, out, lse, nullptr, nullptr,
+                  recall_score, theta, call_list, call_count, stream);
 }
 
 oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch, const float* recall_score,
@@ -349,9 +357,9 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   auto at = [](const void* base, int64_t off) { return static_cast<const char*>(base) + off; };
   // 1) Local pass, every layer.
   for (int32_t l = 0; l < p.L; ++l) {
-    st = run_pass(c, kv, l, batch, false, at(q_local, l * q_layer), at(k_new, l * kv_layer),
+    st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 2) Gate: compaction of the fired requests, counters.
@@ -361,13 +369,14 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   if (rc) return ODA_ERR_HIP;
   // 3) Full recomputation of every layer for the fired requests.
   for (int32_t l = 0; l < p.L; ++l) {
-    st = run_pass(c, kv, l, batch, true, at(qf, l * q_layer), at(k_new, l * kv_layer),
+    st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  list, count, stream);
+                  list, count, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 4) Fused commit of position t for all layers.
-  return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new, c.err, stream));
+  return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new,
+                                       reinterpret_cast<int32_t*>(c.base + c.ws.commit_ticket_off), c.err, stream));
 }
 
 oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t b,
@@ -386,7 +395,7 @@ oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer,
 }
 
 oda_status oda_stage_step(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
-                          const int64_t* step_counter, int64_t num_steps, oda_stream stream) {
+                          int64_t* step_counter, int64_t num_steps, oda_stream stream) {
   if (n < 1 || n > 8 || !src || !dst || !bytes || !step_counter || num_steps < 1) return ODA_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i) {
     if (!src[i] || !dst[i] || bytes[i] < 16 || bytes[i] % 16 != 0) return ODA_ERR_INVALID_ARG;

@@ -10,7 +10,7 @@
 namespace oda {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = 8;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
 constexpr size_t kWsHeader = 256;  // error word, call count, spare
 
@@ -35,7 +35,7 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, part_o_off, part_ml_off, total;
+  size_t err_off, count_off, list_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
   int32_t max_splits;
 };
 
@@ -47,51 +47,51 @@ struct RowSpec {
   int32_t ring_slots;
 };
 
+// Which requests a pass serves.
+enum GateMode : int32_t {
+  kGateAll = 0,     // every active request (Local passes): blockIdx.z is the request id
+  kGateList = 1,    // the compacted list written by the step's gate kernel
+  kGateBallot = 2,  // the pass compacts score > theta itself (standalone gated call)
+};
+
+// One attention pass of one layer: split-K partials, then the last workgroup
+// of each (request, KV head) merges them with the current token.
 struct AttnParams {
   RowSpec rows;
-  int32_t Hq, Hkv, splits, tile_rows;
-  int32_t max_blocks, block_shift;
+  int32_t gate_mode;
+  int32_t batch, Hq, Hkv, splits;
+  int32_t max_blocks, block_shift, capacity;  // capacity = max_blocks * block_size
   int64_t num_blocks;
-  const void* k_base;  // ring of this layer: [max_batch][Hkv][slots][d]; or cache layer base
+  const void* k_base;  // ring of this layer: [max_batch][Hkv][slots][d]; or the cache layer base
   const void* v_base;
   const int32_t* block_table;
   const int32_t* seq_len;
   const int64_t* focus_range;
-  const int32_t* call_list;   // NULL: blockIdx.z is the request id
+  const int32_t* call_list;   // kGateList
   const int32_t* call_count;
+  const float* score;         // kGateBallot
+  float theta;
+  int32_t* call_list_out;     // kGateBallot: optional outputs
+  int32_t* call_count_out;
   const void* q;              // [batch][Hq][d]
+  const void* k_cur;          // [batch][Hkv][d]  the token at position t
+  const void* v_cur;
+  float* out;                 // [batch][Hq][d]
+  float* lse;                 // [batch][Hq] or NULL
   float* part_o;              // [batch][Hq][splits][d]
   float* part_ml;             // [batch][Hq][splits][2]
+  int32_t* tickets;           // [batch][Hkv], zero between launches
   uint32_t* err;
-  float scale_log2;
-  int32_t capacity;           // max_blocks * block_size
-};
-
-struct MergeParams {
-  RowSpec rows;
-  int32_t Hq, Hkv, splits, tile_rows, capacity;
-  const int32_t* seq_len;
-  const int64_t* focus_range;
-  const int32_t* call_list;
-  const int32_t* call_count;
-  const void* q;       // [batch][Hq][d]
-  const void* k_cur;   // [batch][Hkv][d]
-  const void* v_cur;
-  const float* part_o;
-  const float* part_ml;
-  float* out;          // [batch][Hq][d]
-  float* lse;          // [batch][Hq] or NULL
   float scale_log2;
 };
 
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
-int launch_merge(const Plan& p, const MergeParams& m, int32_t batch, oda_stream s);
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
                 int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
                 oda_stream s);
 int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
-                  const void* v_new, uint32_t* err, oda_stream s);
+                  const void* v_new, int32_t* tickets, uint32_t* err, oda_stream s);
 int launch_prefill(const Plan& p, const oda_kv& kv, int32_t batch, int32_t layer,
                    const void* k_src, const void* v_src, int64_t src_rows, uint32_t* err,
                    oda_stream s);
@@ -101,7 +101,7 @@ int launch_access_set(const Plan& p, const oda_kv& kv, int32_t layer, int32_t b,
                       oda_stream s);
 int launch_clear(void* ptr, size_t bytes, oda_stream s);
 int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
-                 const int64_t* counter, int64_t num_steps, oda_stream s);
+                 int64_t* counter, int64_t num_steps, oda_stream s);
 int launch_advance(int64_t* counter, oda_stream s);
 // Rows per workgroup iteration for the attention kernel built for (dtype, d).
 int tile_rows_for(int32_t dtype, int32_t head_dim);

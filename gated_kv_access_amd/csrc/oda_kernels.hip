@@ -6,14 +6,16 @@
 // section "Efficient Execution" (ring KV workspace, fused cross-layer commits,
 // device-side conditional Full pass).
 //
-// Attention is split-K flash decoding.  A workgroup of four wave64s owns one
-// (split, KV head, request) and streams its rows of K and V with 16-byte
-// loads: every lane holds 64 contiguous-in-chunks bytes of a row, so a row of
-// 256 bytes (bf16, d = 128) is spread over 4 lanes and one wave covers 16 rows
-// per pass.  Both query heads of a GQA group use each loaded row.  Scores are
-// reduced across the lanes of a row with DPP, the running maximum is kept per
-// wave (log2 domain, fp32), and each workgroup leaves one (o, m, l) partial per
-// query head; a merge kernel folds the partials and the current token.
+// Attention is split-K flash decoding, one kernel per layer pass.  A workgroup
+// of four wave64s owns one (split, KV head, request) and streams its rows of K
+// and V with 16-byte loads: every lane holds four 16-byte chunks of a row, so a
+// 256-byte row (bf16, d = 128) is spread over 4 lanes and one wave covers 16
+// rows per pass.  All query heads of a GQA group use each loaded row.  Scores
+// are reduced across the lanes of a row with DPP, the running maximum is kept
+// per wave (log2 domain, fp32), and each workgroup leaves one (o, m, l) partial
+// per query head.  The last workgroup of each (request, KV head) to finish --
+// found with a ticket counter in the workspace -- folds the partials and the
+// current token (position t, which the caches do not hold yet) into the output.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -64,6 +66,16 @@ __device__ __forceinline__ float max_over(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Device-coherent (agent scope) stores and loads of the split partials.  On
+// gfx950 they carry the device scope bit, so a partial written on one XCD is
+// read correctly on another without writing back or invalidating any L2.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ----------------------------------------------------------------------------
 // element formats
 
@@ -84,7 +96,7 @@ struct Geo {
   static constexpr int RPP = kWave / LPR;     // rows per wave pass
   static constexpr int EPV = 16 / ES;         // elements per 16-byte vector
   static constexpr int EPL = 4 * EPV;         // elements per lane per row
-  static constexpr int NP = 2;                // passes per wave per tile
+  static constexpr int NP = 1;                // passes per wave per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 8, "row must span 2..8 lanes");
 };
@@ -207,17 +219,6 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
   return iv.lo[2] + row;
 }
 
-__device__ __forceinline__ int32_t pass_rows(const RowSpec& rs, int32_t t, const int64_t* focus_range,
-                                             int32_t b) {
-  if (rs.source == kSrcRing) return ring_rows(t, rs.ring_slots);
-  int64_t fa = 0, fb = 0;
-  if (rs.focus) {
-    fa = focus_range[2 * b];
-    fb = focus_range[2 * b + 1];
-  }
-  return paged_intervals(rs, t, fa, fb).total;
-}
-
 // Splitting n_rows over `splits` workgroups in whole tiles.
 __device__ __forceinline__ void split_tiles(int32_t n_rows, int32_t tile, int32_t splits, int32_t& per,
                                             int32_t& used) {
@@ -227,43 +228,201 @@ __device__ __forceinline__ void split_tiles(int32_t n_rows, int32_t tile, int32_
   used = (n_tiles + per - 1) / per;
 }
 
-// Request handled by blockIdx.z (or merge blockIdx.y): compacted call list or identity.
-__device__ __forceinline__ int32_t request_of(int32_t slot, const int32_t* call_list,
-                                              const int32_t* call_count) {
-  if (call_list == nullptr) return slot;
-  if (slot >= *call_count) return -1;
-  return call_list[slot];
+// ----------------------------------------------------------------------------
+// which request a workgroup serves
+
+// The z-th request (ascending) whose score exceeds theta, found by wave ballots;
+// every wave computes the same answer.  -1 when fewer than z+1 fired.
+__device__ __forceinline__ int32_t ballot_request(const AttnParams& P, int32_t slot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int32_t seen = 0;
+  for (int32_t c = 0; c < P.batch; c += kWave) {
+    const int32_t b = c + lane;
+    const bool fire = b < P.batch && P.seq_len[b] >= 0 && P.score[b] > P.theta;  // NaN never fires
+    const uint64_t mask = __ballot(fire);
+    const int32_t n = __popcll(mask);
+    if (slot < seen + n) {
+      const uint64_t below = mask & ((1ull << lane) - 1ull);
+      const uint64_t hit = __ballot(fire && __popcll(below) == slot - seen);
+      return c + __ffsll((unsigned long long)hit) - 1;
+    }
+    seen += n;
+  }
+  return -1;
+}
+
+// Writes the compacted list of fired requests (ascending, then -1) and its length.
+__device__ void write_call_list(const AttnParams& P) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  int32_t seen = 0;
+  for (int32_t c = 0; c < P.batch; c += kWave) {
+    const int32_t b = c + lane;
+    const bool fire = b < P.batch && P.seq_len[b] >= 0 && P.score[b] > P.theta;
+    const uint64_t mask = __ballot(fire);
+    const uint64_t below = mask & ((1ull << lane) - 1ull);
+    if (fire && P.call_list_out) P.call_list_out[seen + __popcll(below)] = b;
+    seen += __popcll(mask);
+  }
+  if (P.call_list_out)
+    for (int32_t i = seen + lane; i < P.batch; i += kWave) P.call_list_out[i] = -1;
+  if (lane == 0 && P.call_count_out) *P.call_count_out = seen;
 }
 
 // ----------------------------------------------------------------------------
-// split-K partial attention
+// merge of the split partials and the current token (run by one workgroup)
 
-template <int DT, int D, int G, int SRC>
-__global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnParams P) {
+constexpr int kMaxMergeSplits = 512;
+
+// Phase A loads every (m, l) of the `used` partials into LDS in one round and
+// computes the current token's score; phase B turns them into weights; phase C
+// spreads the partial-o reads over split lanes (16 loads in flight per thread)
+// and folds the lanes through LDS.
+template <int DT, int D, int G>
+__device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t used) {
+  constexpr int ES = DT == ODA_BF16 ? 2 : 4;
+  constexpr int EPT = D / kWave;
+  constexpr int GD = G * D;
+  constexpr int SL = kGroupThreads / GD;  // split lanes per output
+  static_assert(SL >= 1 && SL * GD == kGroupThreads, "outputs must tile the workgroup");
+  __shared__ float s_cur[G], s_wcur[G], s_L[G];
+  __shared__ float s_m[G][kMaxMergeSplits];
+  __shared__ float s_l[G][kMaxMergeSplits];
+  __shared__ float s_red[SL][GD];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
+
+  // A: this thread's first 16 partial outputs, the partial maxima and sums,
+  // and the current-token scores -- all loads issued before any is used.
+  const int o_idx = tid % GD, o_sl = tid / GD;
+  const int o_h = o_idx / D, o_e = o_idx % D;
+  const float* po = P.part_o + (head0 + o_h) * P.splits * D + o_e;
+  float x[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int i = o_sl + u * SL;
+    x[u] = i < used ? collect(po + (int64_t)i * D) : 0.f;
+  }
+  for (int idx = tid; idx < G * used; idx += kGroupThreads) {
+    const int h = idx / used, i = idx % used;
+    const float* ml = P.part_ml + ((head0 + h) * P.splits + i) * 2;
+    s_m[h][i] = collect(ml);
+    s_l[h][i] = collect(ml + 1);
+  }
+  for (int h = wave; h < G; h += kWavesPerGroup) {
+    const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * ES;
+    const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) {
+      const int e = lane * EPT + c;
+      float qx, kx;
+      if constexpr (DT == ODA_BF16) {
+        qx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[e] << 16);
+        kx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[e] << 16);
+      } else {
+        qx = reinterpret_cast<const float*>(qrow)[e];
+        kx = reinterpret_cast<const float*>(krow)[e];
+      }
+      dot = fmaf(qx, kx, dot);
+    }
+    dot = sum_over<1, 32>(dot);
+    if (lane == 0) s_cur[h] = dot * P.scale_log2;
+  }
+  __syncthreads();
+
+  // B: M = max over partials and the current token; weights exp2(m_i - M)
+  for (int h = wave; h < G; h += kWavesPerGroup) {
+    float mx = s_cur[h];
+    for (int i = lane; i < used; i += kWave) mx = fmaxf(mx, s_m[h][i]);
+    mx = max_over<1, 32>(mx);
+    float lsum = 0.f;
+    for (int i = lane; i < used; i += kWave) {
+      const float mi = s_m[h][i];
+      const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - mx);
+      s_m[h][i] = w;
+      lsum = fmaf(w, s_l[h][i], lsum);
+    }
+    lsum = sum_over<1, 32>(lsum);
+    if (lane == 0) {
+      const float wc = fast_exp2(s_cur[h] - mx);
+      s_wcur[h] = wc;
+      s_L[h] = lsum + wc;
+      s_cur[h] = mx;  // keep M for the lse
+    }
+  }
+  __syncthreads();
+
+  // C: weighted sum of the partial outputs
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = o_sl + u * SL;
+      if (i < used) acc = fmaf(s_m[o_h][i], x[u], acc);
+    }
+    for (int i = o_sl + 16 * SL; i < used; i += SL) acc = fmaf(s_m[o_h][i], collect(po + (int64_t)i * D), acc);
+    s_red[o_sl][o_idx] = acc;
+  }
+  __syncthreads();
+  if (tid < GD) {
+    const int h = tid / D, e = tid % D;
+    float acc = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) acc += s_red[sl][tid];
+    const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+    float vx;
+    if constexpr (DT == ODA_BF16) vx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
+    else vx = reinterpret_cast<const float*>(vrow)[e];
+    acc = fmaf(s_wcur[h], vx, acc);
+    P.out[(head0 + h) * D + e] = acc / s_L[h];
+  }
+  if (P.lse != nullptr && tid < G) P.lse[head0 + tid] = (s_cur[tid] + __log2f(s_L[tid])) * kLn2;
+}
+
+// ----------------------------------------------------------------------------
+// one attention pass of one layer: split-K partials + last-workgroup merge
+
+template <int DT, int D, int G, int SRC, bool BALLOT>
+__global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
   using Gm = Geo<DT, D>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int TILE = Gm::TILE;
   constexpr int ES = Gm::ES;
 
-  const int32_t b = request_of(blockIdx.z, P.call_list, P.call_count);
-  if (b < 0) return;
-  const int32_t committed = P.seq_len[b];
-  if (committed < 0) return;
-  const int32_t t = committed + 1;
-  if (SRC == kSrcPaged && t - 1 > P.capacity) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
-    return;
+  int32_t b;
+  if constexpr (BALLOT) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) write_call_list(P);
+    b = ballot_request(P, blockIdx.z);
+  } else if (P.gate_mode == kGateList) {
+    b = (int32_t)blockIdx.z < *P.call_count ? P.call_list[blockIdx.z] : -1;
+  } else {
+    b = blockIdx.z;
   }
+  if (b < 0) return;
   const int32_t g = blockIdx.y;
   const int32_t split = blockIdx.x;
 
+  // Ring passes scan every slot of the ring whatever t is, so their first tile
+  // loads need no per-request state and go out before seq_len arrives; which
+  // slots belong to S^L_t is decided per row once t is known.  Paged passes
+  // need t (and the block table) to know what to read.
+  int32_t t = 0;
   RingState rst{};
   Intervals iv{};
   int32_t n_rows;
   if constexpr (SRC == kSrcRing) {
-    rst = ring_state(t, P.rows.sink, P.rows.window);
-    n_rows = ring_rows(t, P.rows.ring_slots);
+    n_rows = P.rows.ring_slots;
   } else {
+    const int32_t committed = P.seq_len[b];
+    if (committed < 0) return;
+    t = committed + 1;
+    if (t - 1 > P.capacity) {
+      if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+      return;
+    }
     int64_t fa = 0, fb = 0;
     if (P.rows.focus) {
       fa = P.focus_range[2 * b];
@@ -274,6 +433,10 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
   }
   int32_t per, used;
   split_tiles(n_rows, TILE, P.splits, per, used);
+  if (used == 0) {  // t = 1 on a paged pass: only the current token
+    if (split == 0) merge_and_write<DT, D, G>(P, b, g, 0);
+    return;
+  }
   if (split >= used) return;
   const int32_t tile_begin = split * per;
   const int32_t tile_end = min(tile_begin + per, (n_rows + TILE - 1) / TILE);
@@ -311,26 +474,46 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
   }
 
-  for (int32_t tile = tile_begin; tile < tile_end; ++tile) {
-    uint4 kr[NP][4], vr[NP][4];
-    bool valid[NP];
+  // Tile registers: K and V of NP passes plus their validity.  Two sets
+  // ping-pong so the loads of tile i+1 are in flight while tile i is reduced.
+  struct TileRegs {
+    uint4 k[NP][4];
+    uint4 v[NP][4];
+    bool valid[NP];  // paged: row in the pass; ring: row inside the ring (membership checked later)
+    int32_t row[NP];
+  };
+  // Paged rows: the physical block of each lane's row, looked up two tiles
+  // before its K/V loads so the dependent block-table read is never waited on.
+  // -1 marks a row outside the pass (or a block id the table gets wrong).
+  struct BlockIds {
+    int32_t blk[NP];
+  };
+  auto resolve_blocks = [&](int32_t tile, BlockIds& B) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      B.blk[i] = -1;
+      if constexpr (SRC == kSrcPaged) {
+        const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
+        if (tile < tile_end && row < n_rows) {
+          const int32_t p = interval_position(iv, row);
+          B.blk[i] = btab[(p - 1) >> P.block_shift];
+        }
+      }
+    }
+  };
+  auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
+      R.row[i] = row;
       bool ok = row < n_rows;
       int64_t off = 0;
       if constexpr (SRC == kSrcRing) {
-        if (ok) {
-          bool in_local;
-          ring_slot_position(rst, row, in_local);
-          ok = in_local;
-          off = ring_head_off + (int64_t)row * D * ES;
-        }
+        off = ring_head_off + (int64_t)row * D * ES;
       } else {
         if (ok) {
-          const int32_t p = interval_position(iv, row);
-          const int32_t r0 = p - 1;
-          const int32_t blk = btab[r0 >> P.block_shift];
+          const int32_t r0 = interval_position(iv, row) - 1;
+          const int32_t blk = B.blk[i];
           if (blk < 0 || (int64_t)blk >= P.num_blocks) {
             atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
             ok = false;
@@ -339,19 +522,34 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
           }
         }
       }
-      valid[i] = ok;
+      R.valid[i] = ok;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (ok) {
-          kr[i][j] = *reinterpret_cast<const uint4*>(kbase + off + (j * LPR + sub) * 16);
-          vr[i][j] = *reinterpret_cast<const uint4*>(vbase + off + (j * LPR + sub) * 16);
+          R.k[i][j] = *reinterpret_cast<const uint4*>(kbase + off + (j * LPR + sub) * 16);
+          R.v[i][j] = *reinterpret_cast<const uint4*>(vbase + off + (j * LPR + sub) * 16);
         } else {
-          kr[i][j] = make_uint4(0, 0, 0, 0);
-          vr[i][j] = make_uint4(0, 0, 0, 0);
+          R.k[i][j] = make_uint4(0, 0, 0, 0);
+          R.v[i][j] = make_uint4(0, 0, 0, 0);
         }
       }
     }
+  };
 
+  auto process_tile = [&](TileRegs& R) {
+    if constexpr (SRC == kSrcRing) {
+      // Membership in S^L_t; rows outside it never reach the sums (slots not
+      // yet written may hold anything, so their values are replaced by zeros).
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        bool in_local = false;
+        if (R.valid[i]) ring_slot_position(rst, R.row[i], in_local);
+        R.valid[i] = in_local;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (!in_local) R.v[i][j] = make_uint4(0, 0, 0, 0);
+      }
+    }
     // scores s = scale*log2(e) * <q_h, k_row>
     float s[NP][G];
 #pragma unroll
@@ -361,7 +559,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 kk = kr[i][j];
+          const uint4 kk = R.k[i][j];
           const uint4 qq = qv[h][j];
           if constexpr (DT == ODA_BF16) {
             acc = dot2_bf16(kk.x, qq.x, acc);
@@ -376,7 +574,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
           }
         }
         acc = sum_over<1, LPR / 2>(acc);
-        s[i][h] = valid[i] ? acc * P.scale_log2 : -INFINITY;
+        s[i][h] = R.valid[i] ? acc * P.scale_log2 : -INFINITY;
       }
     }
 
@@ -403,12 +601,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
       float pr[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        pr[h] = valid[i] ? fast_exp2(s[i][h] - m_run[h]) : 0.f;
+        pr[h] = R.valid[i] ? fast_exp2(s[i][h] - m_run[h]) : 0.f;
         l_acc[h] += pr[h];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w4[4] = {vr[i][j].x, vr[i][j].y, vr[i][j].z, vr[i][j].w};
+        const uint32_t w4[4] = {R.v[i][j].x, R.v[i][j].y, R.v[i][j].z, R.v[i][j].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if constexpr (DT == ODA_BF16) {
@@ -427,6 +625,27 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
         }
       }
     }
+  };
+
+  TileRegs ra, rb;
+  BlockIds ba, bb;
+  resolve_blocks(tile_begin, ba);
+  resolve_blocks(tile_begin + 1, bb);
+  load_tile(tile_begin, ba, ra);
+  if constexpr (SRC == kSrcRing) {
+    const int32_t committed = P.seq_len[b];
+    if (committed < 0) return;
+    t = committed + 1;
+    rst = ring_state(t, P.rows.sink, P.rows.window);
+  }
+  for (int32_t tile = tile_begin; tile < tile_end; tile += 2) {
+    const bool has_b = tile + 1 < tile_end;
+    resolve_blocks(tile + 2, ba);
+    if (has_b) load_tile(tile + 1, bb, rb);
+    process_tile(ra);
+    resolve_blocks(tile + 3, bb);
+    if (tile + 2 < tile_end) load_tile(tile + 2, ba, ra);
+    if (has_b) process_tile(rb);
   }
 
   // wave epilogue: fold the row groups (lanes that share `sub`)
@@ -440,6 +659,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
   __shared__ float s_o[kWavesPerGroup][G][D];
   __shared__ float s_m[kWavesPerGroup][G];
   __shared__ float s_l[kWavesPerGroup][G];
+  __shared__ int32_t s_last;
   if (rrow == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -472,79 +692,29 @@ __global__ __launch_bounds__(kGroupThreads) void attention_partial_kernel(AttnPa
       }
     }
     const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
-    P.part_o[row * D + e] = acc;
+    publish(P.part_o + row * D + e, acc);
     if (e == 0) {
-      P.part_ml[row * 2 + 0] = M;
-      P.part_ml[row * 2 + 1] = lsum;
+      publish(P.part_ml + row * 2 + 0, M);
+      publish(P.part_ml + row * 2 + 1, lsum);
     }
   }
-}
 
-// ----------------------------------------------------------------------------
-// log-sum-exp merge of the partials and the current token
-
-template <int DT, int D>
-__global__ __launch_bounds__(kWave) void merge_kernel(MergeParams P) {
-  constexpr int ES = DT == ODA_BF16 ? 2 : 4;
-  constexpr int EPT = D / kWave;  // elements per lane (1 or 2)
-  const int32_t b = request_of(blockIdx.y, P.call_list, P.call_count);
-  if (b < 0) return;
-  const int32_t committed = P.seq_len[b];
-  if (committed < 0) return;
-  const int32_t t = committed + 1;
-  if (P.rows.source == kSrcPaged && t - 1 > P.capacity) return;
-  const int32_t h = blockIdx.x;
-  const int32_t g = h / (P.Hq / P.Hkv);
-  const int lane = threadIdx.x;
-
-  const int32_t n_rows = pass_rows(P.rows, t, P.focus_range, b);
-  int32_t per, used;
-  split_tiles(n_rows, P.tile_rows, P.splits, per, used);
-  if (n_rows == 0) used = 0;
-
-  float qx[EPT], kx[EPT], vx[EPT];
-  const char* qrow = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + h) * D * ES;
-  const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-  const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) {
-    const int e = lane * EPT + c;
-    if constexpr (DT == ODA_BF16) {
-      qx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[e] << 16);
-      kx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[e] << 16);
-      vx[c] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
-    } else {
-      qx[c] = reinterpret_cast<const float*>(qrow)[e];
-      kx[c] = reinterpret_cast<const float*>(krow)[e];
-      vx[c] = reinterpret_cast<const float*>(vrow)[e];
-    }
+  // The last workgroup of this (request, KV head) to finish merges.  Every
+  // wave waits until its device-scope partial stores have completed, then one
+  // thread takes a ticket; the holder of the last ticket reads all partials
+  // with device-scope loads.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t prev = __hip_atomic_fetch_add(&P.tickets[(int64_t)b * P.Hkv + g], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == used - 1;
   }
-  float dot = 0.f;
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) dot = fmaf(qx[c], kx[c], dot);
-  dot = sum_over<1, 32>(dot);
-  const float s_cur = dot * P.scale_log2;
-
-  const int64_t row0 = ((int64_t)b * P.Hq + h) * P.splits;
-  float M = s_cur;
-  for (int i = 0; i < used; ++i) M = fmaxf(M, P.part_ml[(row0 + i) * 2]);
-  float lsum = fast_exp2(s_cur - M);
-  float acc[EPT];
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) acc[c] = lsum * vx[c];
-  for (int i = 0; i < used; ++i) {
-    const float mi = P.part_ml[(row0 + i) * 2];
-    const float li = P.part_ml[(row0 + i) * 2 + 1];
-    const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
-    lsum = fmaf(w, li, lsum);
-#pragma unroll
-    for (int c = 0; c < EPT; ++c) acc[c] = fmaf(w, P.part_o[(row0 + i) * D + lane * EPT + c], acc[c]);
-  }
-  const float inv = 1.f / lsum;
-  float* orow = P.out + ((int64_t)b * P.Hq + h) * D;
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) orow[lane * EPT + c] = acc[c] * inv;
-  if (P.lse != nullptr && lane == 0) P.lse[(int64_t)b * P.Hq + h] = (M + __log2f(lsum)) * kLn2;
+  __syncthreads();
+  if (!s_last) return;
+  merge_and_write<DT, D, G>(P, b, g, used);
+  if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
+    __hip_atomic_store(&P.tickets[(int64_t)b * P.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------
@@ -656,26 +826,32 @@ struct CommitParams {
   int32_t* swring_pos;
   const int32_t* block_table;
   int32_t* seq_len;
+  int32_t* tickets;  // [batch], zero between launches
   uint32_t* err;
 };
 
+// grid (layer, request): each workgroup writes one layer of one request; the
+// last workgroup of a request (ticket) records t in the ring-slot table and
+// advances seq_len, after every workgroup of that request has read it.
 __global__ __launch_bounds__(256) void commit_kernel(CommitParams P) {
-  const int32_t b = blockIdx.x;
-  if (b >= P.batch) return;
+  const int32_t l = blockIdx.x;
+  const int32_t b = blockIdx.y;
   const int32_t committed = P.seq_len[b];
   if (committed < 0) return;
   const int32_t t = committed + 1;
   const int64_t cap = (int64_t)P.max_blocks << P.block_shift;
   const bool has_gated = P.n_layers_gated > 0;
+  // The checks below give the same answer in every workgroup of request b, so
+  // either all of them take a ticket or none does.
   if (has_gated && t > cap) {
-    if (threadIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
+    if (threadIdx.x == 0 && l == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
     return;
   }
   int32_t blk = 0;
   if (has_gated) {
     blk = P.block_table[(int64_t)b * P.max_blocks + ((t - 1) >> P.block_shift)];
     if (blk < 0 || (int64_t)blk >= P.num_blocks) {
-      if (threadIdx.x == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
+      if (threadIdx.x == 0 && l == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
       return;
     }
   }
@@ -684,17 +860,14 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams P) {
   const int32_t sslot = P.sw_window > 0 ? (t - 1) % P.sw_window : 0;
   const int64_t row_bytes = (int64_t)P.D * P.esize;
   const int32_t vecs = (int32_t)(row_bytes / 16);
-  const int32_t per_layer = P.Hkv * vecs;
-
-  for (int32_t idx = threadIdx.x; idx < P.L * per_layer; idx += blockDim.x) {
-    const int32_t l = idx / per_layer;
-    const int32_t rem = idx % per_layer;
-    const int32_t h = rem / vecs, vi = rem % vecs;
+  const int64_t rank = P.kidx[l];
+  const bool gated = P.kind[l] == ODA_LAYER_GATED;
+  for (int32_t idx = threadIdx.x; idx < P.Hkv * vecs; idx += blockDim.x) {
+    const int32_t h = idx / vecs, vi = idx % vecs;
     const int64_t src = (((int64_t)l * P.batch + b) * P.Hkv + h) * row_bytes + vi * 16;
     const uint4 kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_new) + src);
     const uint4 vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_new) + src);
-    const int64_t rank = P.kidx[l];
-    if (P.kind[l] == ODA_LAYER_GATED) {
+    if (gated) {
       const int64_t coff = ((((rank * P.num_blocks + blk) * P.Hkv + h) << P.block_shift) + in_blk) * row_bytes + vi * 16;
       *reinterpret_cast<uint4*>(static_cast<char*>(P.k_cache) + coff) = kx;
       *reinterpret_cast<uint4*>(static_cast<char*>(P.v_cache) + coff) = vx;
@@ -707,11 +880,18 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams P) {
       *reinterpret_cast<uint4*>(static_cast<char*>(P.v_swring) + roff) = vx;
     }
   }
+  __shared__ int32_t s_last;
   __syncthreads();
   if (threadIdx.x == 0) {
+    const int32_t prev = __hip_atomic_fetch_add(&P.tickets[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == P.L - 1;
+  }
+  __syncthreads();
+  if (s_last && threadIdx.x == 0) {
     if (has_gated) P.ring_pos[(int64_t)b * P.ring_slots + gslot] = t;
     if (P.n_layers_sliding > 0) P.swring_pos[(int64_t)b * P.sw_window + sslot] = t;
     P.seq_len[b] = t;
+    __hip_atomic_store(&P.tickets[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -889,10 +1069,12 @@ struct StageParams {
   const void* src[8];
   void* dst[8];
   int64_t bytes[8];
-  const int64_t* counter;
+  int64_t* counter;  // [0] step index, [1] ticket (zero between launches)
   int64_t num_steps;
 };
 
+// Copies step k's inputs (k = counter[0] mod num_steps); the last workgroup to
+// finish -- after every workgroup has read k -- advances counter[0].
 __global__ __launch_bounds__(256) void stage_kernel(StageParams P) {
   const int64_t k = *P.counter % P.num_steps;
   for (int i = 0; i < P.n; ++i) {
@@ -901,6 +1083,17 @@ __global__ __launch_bounds__(256) void stage_kernel(StageParams P) {
     uint4* d = reinterpret_cast<uint4*>(P.dst[i]);
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < vecs; v += (int64_t)gridDim.x * blockDim.x)
       d[v] = s[v];
+  }
+  __shared__ int32_t s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t prev = __hip_atomic_fetch_add(P.counter + 1, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (int64_t)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (s_last && threadIdx.x == 0) {
+    P.counter[0] += 1;
+    __hip_atomic_store(P.counter + 1, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -914,10 +1107,14 @@ __global__ void advance_kernel(int64_t* counter) {
 template <int DT, int D, int G>
 int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   dim3 grid(a.splits, a.Hkv, batch);
-  if (a.rows.source == kSrcRing)
-    hipLaunchKernelGGL((attention_partial_kernel<DT, D, G, kSrcRing>), grid, dim3(kGroupThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attention_partial_kernel<DT, D, G, kSrcPaged>), grid, dim3(kGroupThreads), 0, s, a);
+  const bool ballot = a.gate_mode == kGateBallot;
+  if (a.rows.source == kSrcRing) {
+    if (ballot) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true>), grid, dim3(kGroupThreads), 0, s, a);
+    else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, false>), grid, dim3(kGroupThreads), 0, s, a);
+  } else {
+    if (ballot) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, true>), grid, dim3(kGroupThreads), 0, s, a);
+    else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, false>), grid, dim3(kGroupThreads), 0, s, a);
+  }
   return (int)hipGetLastError();
 }
 
@@ -946,19 +1143,6 @@ int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stre
   }
   if (p.D == 128) return launch_attention_d<ODA_F32, 128>(p, a, batch, s);
   return launch_attention_d<ODA_F32, 64>(p, a, batch, s);
-}
-
-int launch_merge(const Plan& p, const MergeParams& m, int32_t batch, oda_stream s) {
-  if (batch <= 0) return 0;
-  dim3 grid(p.Hq, batch);
-  if (p.dtype == ODA_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((merge_kernel<ODA_BF16, 128>), grid, dim3(kWave), 0, s, m);
-    else hipLaunchKernelGGL((merge_kernel<ODA_BF16, 64>), grid, dim3(kWave), 0, s, m);
-  } else {
-    if (p.D == 128) hipLaunchKernelGGL((merge_kernel<ODA_F32, 128>), grid, dim3(kWave), 0, s, m);
-    else hipLaunchKernelGGL((merge_kernel<ODA_F32, 64>), grid, dim3(kWave), 0, s, m);
-  }
-  return (int)hipGetLastError();
 }
 
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
@@ -993,7 +1177,7 @@ int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* sco
 }
 
 int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
-                  const void* v_new, uint32_t* err, oda_stream s) {
+                  const void* v_new, int32_t* tickets, uint32_t* err, oda_stream s) {
   if (batch <= 0) return 0;
   CommitParams c{};
   c.L = p.L;
@@ -1027,8 +1211,9 @@ int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_
   c.swring_pos = kv.swring_pos;
   c.block_table = kv.block_table;
   c.seq_len = kv.seq_len;
+  c.tickets = tickets;
   c.err = err;
-  hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(256), 0, s, c);
+  hipLaunchKernelGGL(commit_kernel, dim3(p.L, batch), dim3(256), 0, s, c);
   return (int)hipGetLastError();
 }
 
@@ -1140,7 +1325,7 @@ int launch_clear(void* ptr, size_t bytes, oda_stream s) {
 }
 
 int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
-                 const int64_t* counter, int64_t num_steps, oda_stream s) {
+                 int64_t* counter, int64_t num_steps, oda_stream s) {
   StageParams sp{};
   sp.n = n;
   int64_t most = 0;

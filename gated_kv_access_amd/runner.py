@@ -1,9 +1,9 @@
 """Replays whole ODA decode steps from pre-generated per-step inputs.
 
 One replayed step is: oda_stage_step (copy step k's q / k_new / v_new / score
-into fixed buffers, k read from a device counter), oda_step (Local pass of
-every layer, gate, gated Full pass of every layer, fused commit), and
-oda_advance_counter.  Captured once into a HIP graph (through
+into fixed buffers, k read from a device counter that the same kernel then
+advances) and oda_step (Local pass of every layer, gate, gated Full pass of
+every layer, fused commit).  Captured once into a HIP graph (through
 torch.cuda.CUDAGraph, which records the library's launches on the capture
 stream), the step then runs with no host round trip: the gate decision never
 leaves the device, and skipped requests launch no Full work beyond the
@@ -55,11 +55,10 @@ class StepRunner:
 
     def _step(self) -> None:
         st = self.st
-        B.stage_step(self.src, self.dst, self.step_counter, self.num_steps)
+        B.stage_step(self.src, self.dst, self.step_counter, self.num_steps)  # also advances the counter
         B.step(st.dims, st.kv, st.wl.batch, self.q_buf, self.qf_buf, self.k_buf, self.v_buf, self.score_buf,
                self.theta, self.out, self.lse, self.call_list, self.call_count, self.full_calls, self.counters,
                st.workspace)
-        B.advance_counter(self.step_counter)
 
     def step_eager(self) -> None:
         self._step()

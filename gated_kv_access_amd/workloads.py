@@ -43,6 +43,7 @@ class Workload:
     score_mode: str = "normal"      # "normal" | "rho_minus_u" | "exact"
     rho: Tuple[float, ...] = (0.5,)  # per request (one value = all requests)
     seed: int = 0
+    block_order: str = "shuffled"   # physical block ids: "shuffled" (seeded permutation) or "sequential"
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -197,7 +198,10 @@ def gen_block_table(wl: Workload, spare_blocks: int = 0) -> Tuple[np.ndarray, in
     need = [wl.blocks_for(b) for b in range(wl.batch)]
     total = int(sum(need)) + spare_blocks
     rng = np.random.default_rng([wl.seed, 23])
-    perm = rng.permutation(total).astype(np.int32)
+    if wl.block_order == "sequential":
+        perm = np.arange(total, dtype=np.int32)
+    else:
+        perm = rng.permutation(total).astype(np.int32)
     table = -np.ones((wl.batch, wl.max_blocks_per_seq), dtype=np.int32)
     off = 0
     for b in range(wl.batch):

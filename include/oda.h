@@ -123,8 +123,10 @@ typedef struct {
  * first 256 bytes hold the device error word).  0 on invalid dims. */
 size_t oda_workspace_size(const oda_dims* dims, int32_t batch);
 
-/* Clears the workspace's error word and counters (a small kernel; call once
- * after allocating a workspace).  The workspace needs no other initialisation. */
+/* Zeroes the workspace (a small kernel; call once after allocating it).  The
+ * kernels keep ticket words there that must read zero between launches (they
+ * find the last workgroup of a request with them and reset them), next to the
+ * error word and the split partials. */
 oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspace,
                               size_t workspace_bytes, oda_stream stream);
 
@@ -208,15 +210,18 @@ oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer,
                           void* workspace, size_t workspace_bytes, oda_stream stream);
 
 /* Input staging for replayed graphs: for i < n copies bytes[i] bytes from
- * src[i] + k*bytes[i] to dst[i], where k = *step_counter mod num_steps.
- * src, dst and bytes are HOST arrays of n <= 8 entries (their values are
- * baked into the launch); the buffers they point to are device memory and
- * every bytes[i] must be a multiple of 16. */
+ * src[i] + k*bytes[i] to dst[i], where k = step_counter[0] mod num_steps, then
+ * advances step_counter[0] by one.  step_counter points to two device int64:
+ * the step index and a word the kernel uses to find its last workgroup (zero
+ * before the first call; the kernel leaves it zero).  src, dst and bytes are
+ * HOST arrays of n <= 8 entries (their values are baked into the launch); the
+ * buffers they point to are device memory and every bytes[i] must be a
+ * multiple of 16. */
 oda_status oda_stage_step(int32_t n, const void* const* src, void* const* dst,
-                          const int64_t* bytes, const int64_t* step_counter, int64_t num_steps,
+                          const int64_t* bytes, int64_t* step_counter, int64_t num_steps,
                           oda_stream stream);
 
-/* *step_counter += 1 (one tiny kernel; the last node of a replayed step). */
+/* step_counter[0] += 1 (one tiny kernel). */
 oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream);
 
 /* Host.  Human-readable status name. */
