@@ -127,7 +127,8 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.err_off = 0;
   w.count_off = 4;
   w.list_off = oda::kWsHeader;
-  w.ticket_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
   w.commit_ticket_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
   w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
@@ -183,8 +184,9 @@ oda_status hip_status(int rc) { return rc == 0 ? ODA_OK : ODA_ERR_HIP; }
 // (Full pass that compacts score > theta itself).
 oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, int32_t gate,
                     const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
-                    const int32_t* call_list, const int32_t* call_count, const float* score,
-                    float theta, int32_t* list_out, int32_t* count_out, oda_stream s) {
+                    const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
+                    const float* score, float theta, int32_t* list_out, int32_t* count_out,
+                    oda_stream s) {
   const Plan& p = c.plan;
   const bool gated = p.kind[layer] == ODA_LAYER_GATED;
   const bool full = gate != oda::kGateAll;
@@ -219,6 +221,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.focus_range = kv->focus_range;
   a.call_list = call_list;
   a.call_count = call_count;
+  a.call_len = call_len;
   a.score = score;
   a.theta = theta;
   a.call_list_out = list_out;
@@ -301,7 +304,7 @@ oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t laye
   st = check_kv(c.plan, kv, false, true);
   if (st != ODA_OK) return st;
   return run_pass(c, kv, layer, batch, oda::kGateAll, q, k_cur, v_cur, out, lse, nullptr, nullptr, nullptr,
-                  0.f, nullptr, nullptr, stream);
+                  nullptr, 0.f, nullptr, nullptr, stream);
 }
 
 oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
@@ -319,7 +322,7 @@ oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t
   st = check_kv(c.plan, kv, gated, !gated);
   if (st != ODA_OK) return st;
   return run_pass(c, kv, layer, batch, oda::kGateBallot, q, k_cur, v_cur, out, lse, nullptr, nullptr,
-                  recall_score, theta, call_list, call_count, stream);
+                  nullptr, recall_score, theta, call_list, call_count, stream);
 }
 
 oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch, const float* recall_score,
@@ -331,7 +334,7 @@ oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   if (!recall_score || isnan(theta) || !kv || !kv->seq_len) return ODA_ERR_INVALID_ARG;
   if (c.plan.focus && c.plan.Lg > 0 && counters && !kv->focus_range) return ODA_ERR_INVALID_ARG;
   return hip_status(oda::launch_gate(c.plan, *kv, batch, recall_score, theta, call_list, call_count,
-                                     full_calls, counters, stream));
+                                     nullptr, full_calls, counters, stream));
 }
 
 oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const void* q_local,
@@ -359,19 +362,21 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   for (int32_t l = 0; l < p.L; ++l) {
     st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 2) Gate: compaction of the fired requests, counters.
   int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
   int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
-  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, full_calls, counters, stream);
+  int32_t* lens = reinterpret_cast<int32_t*>(c.base + c.ws.len_off);
+  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, lens, full_calls, counters,
+                            stream);
   if (rc) return ODA_ERR_HIP;
   // 3) Full recomputation of every layer for the fired requests.
   for (int32_t l = 0; l < p.L; ++l) {
     st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  list, count, nullptr, 0.f, nullptr, nullptr, stream);
+                  list, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 4) Fused commit of position t for all layers.

@@ -35,7 +35,7 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
+  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
   int32_t max_splits;
 };
 
@@ -69,6 +69,7 @@ struct AttnParams {
   const int64_t* focus_range;
   const int32_t* call_list;   // kGateList
   const int32_t* call_count;
+  const int32_t* call_len;    // kGateList: committed length of each listed request
   const float* score;         // kGateBallot
   float theta;
   int32_t* call_list_out;     // kGateBallot: optional outputs
@@ -88,8 +89,8 @@ struct AttnParams {
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
-                int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
-                oda_stream s);
+                int32_t* call_list, int32_t* call_count, int32_t* call_len, int64_t* full_calls,
+                int64_t* counters, oda_stream s);
 int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
                   const void* v_new, int32_t* tickets, uint32_t* err, oda_stream s);
 int launch_prefill(const Plan& p, const oda_kv& kv, int32_t batch, int32_t layer,

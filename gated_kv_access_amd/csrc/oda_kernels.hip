@@ -66,6 +66,37 @@ __device__ __forceinline__ float max_over(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotate right by N lanes inside each row of 16 lanes (DPP, a VALU operand
+// modifier: no LDS traffic and no wait).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum / max over the lanes of a 16-lane row that are congruent modulo STEP
+// (the row groups when a K/V row spans STEP lanes).
+template <int STEP>
+__device__ __forceinline__ float row_group_sum(float v) {
+  if constexpr (STEP <= 8) v += row_ror<8>(v);
+  if constexpr (STEP <= 4) v += row_ror<4>(v);
+  if constexpr (STEP <= 2) v += row_ror<2>(v);
+  if constexpr (STEP <= 1) v += row_ror<1>(v);
+  return v;
+}
+template <int STEP>
+__device__ __forceinline__ float row_group_max(float v) {
+  if constexpr (STEP <= 8) v = fmaxf(v, row_ror<8>(v));
+  if constexpr (STEP <= 4) v = fmaxf(v, row_ror<4>(v));
+  if constexpr (STEP <= 2) v = fmaxf(v, row_ror<2>(v));
+  if constexpr (STEP <= 1) v = fmaxf(v, row_ror<1>(v));
+  return v;
+}
+
+// A lane rescales its running sums only when a score exceeds its reference
+// maximum by more than this (log2 domain): weights stay below 2^8, far from
+// fp32 overflow, and the result is exact whatever the reference is.
+constexpr float kRescaleGap = 8.f;
+
 // Device-coherent (agent scope) stores and loads of the split partials.  On
 // gfx950 they carry the device scope bit, so a partial written on one XCD is
 // read correctly on another without writing back or invalidating any L2.
@@ -232,19 +263,23 @@ __device__ __forceinline__ void split_tiles(int32_t n_rows, int32_t tile, int32_
 // which request a workgroup serves
 
 // The z-th request (ascending) whose score exceeds theta, found by wave ballots;
-// every wave computes the same answer.  -1 when fewer than z+1 fired.
-__device__ __forceinline__ int32_t ballot_request(const AttnParams& P, int32_t slot) {
+// every wave computes the same answer.  -1 when fewer than z+1 fired.  Also
+// returns the request's committed length, read in the same round trip.
+__device__ __forceinline__ int32_t ballot_request(const AttnParams& P, int32_t slot, int32_t& committed) {
   const int lane = threadIdx.x & (kWave - 1);
   int32_t seen = 0;
   for (int32_t c = 0; c < P.batch; c += kWave) {
     const int32_t b = c + lane;
-    const bool fire = b < P.batch && P.seq_len[b] >= 0 && P.score[b] > P.theta;  // NaN never fires
+    const int32_t len = b < P.batch ? P.seq_len[b] : -1;
+    const bool fire = len >= 0 && P.score[b] > P.theta;  // NaN never fires
     const uint64_t mask = __ballot(fire);
     const int32_t n = __popcll(mask);
     if (slot < seen + n) {
       const uint64_t below = mask & ((1ull << lane) - 1ull);
       const uint64_t hit = __ballot(fire && __popcll(below) == slot - seen);
-      return c + __ffsll((unsigned long long)hit) - 1;
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      committed = __shfl(len, src, kWave);
+      return c + src;
     }
     seen += n;
   }
@@ -392,12 +427,16 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   constexpr int TILE = Gm::TILE;
   constexpr int ES = Gm::ES;
 
+  // The request this workgroup serves and its committed length (-1 = none).
   int32_t b;
+  int32_t committed = -1;
   if constexpr (BALLOT) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) write_call_list(P);
-    b = ballot_request(P, blockIdx.z);
+    b = ballot_request(P, blockIdx.z, committed);
   } else if (P.gate_mode == kGateList) {
-    b = (int32_t)blockIdx.z < *P.call_count ? P.call_list[blockIdx.z] : -1;
+    const bool in_list = (int32_t)blockIdx.z < *P.call_count;
+    b = in_list ? P.call_list[blockIdx.z] : -1;
+    committed = in_list ? P.call_len[blockIdx.z] : -1;  // written with the list by the gate
   } else {
     b = blockIdx.z;
   }
@@ -416,7 +455,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   if constexpr (SRC == kSrcRing) {
     n_rows = P.rows.ring_slots;
   } else {
-    const int32_t committed = P.seq_len[b];
+    if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
     t = committed + 1;
     if (t - 1 > P.capacity) {
@@ -578,20 +617,19 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       }
     }
 
-    // running maximum per head, uniform over the wave
+    // Per-lane reference maximum (the LPR lanes of a row agree on it): move it
+    // only when a score would push a weight past 2^kRescaleGap.
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float tm = s[0][h];
+    for (int i = 0; i < NP; ++i) {
 #pragma unroll
-      for (int i = 1; i < NP; ++i) tm = fmaxf(tm, s[i][h]);
-      tm = max_over<LPR, 32>(tm);
-      const float m_new = fmaxf(m_run[h], tm);
-      if (m_new > m_run[h]) {
-        const float alpha = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - m_new);
-        l_acc[h] *= alpha;
+      for (int h = 0; h < G; ++h) {
+        if (s[i][h] > m_run[h] + kRescaleGap) {
+          const float alpha = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - s[i][h]);
+          l_acc[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-        m_run[h] = m_new;
+          for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+          m_run[h] = s[i][h];
+        }
       }
     }
 
@@ -633,7 +671,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   resolve_blocks(tile_begin + 1, bb);
   load_tile(tile_begin, ba, ra);
   if constexpr (SRC == kSrcRing) {
-    const int32_t committed = P.seq_len[b];
+    if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
     t = committed + 1;
     rst = ring_state(t, P.rows.sink, P.rows.window);
@@ -648,54 +686,82 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (has_b) process_tile(rb);
   }
 
-  // wave epilogue: fold the row groups (lanes that share `sub`)
+  // Epilogue 1: inside each 16-lane row, fold the row groups onto a common
+  // maximum with DPP; every lane then holds its row's sums for its `sub`.
+  constexpr int kRows16 = kWave / 16;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l_acc[h] = sum_over<LPR, 32>(l_acc[h]);
+    const float mrow = row_group_max<LPR>(m_run[h]);
+    const float sc = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - mrow);
+    m_run[h] = mrow;
+    l_acc[h] = row_group_sum<LPR>(l_acc[h] * sc);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = sum_over<LPR, 32>(o[h][e]);
+    for (int e = 0; e < EPL; ++e) o[h][e] = row_group_sum<LPR>(o[h][e] * sc);
   }
 
-  __shared__ float s_o[kWavesPerGroup][G][D];
-  __shared__ float s_m[kWavesPerGroup][G];
-  __shared__ float s_l[kWavesPerGroup][G];
+  // Epilogue 2: the first LPR lanes of each 16-lane row hold distinct element
+  // slices; they store the row's sums, and the 8 waves x 4 rows are folded
+  // through LDS into this workgroup's partial, published device-wide.
+  constexpr int NWR = kWavesPerGroup * kRows16;
+  __shared__ float4 s_o4[NWR][G][D / 4];
+  __shared__ float s_m[NWR][G];
+  __shared__ float s_l[NWR][G];
+  __shared__ float s_w[NWR][G];
+  __shared__ float s_M[G], s_Lw[G];
   __shared__ int32_t s_last;
-  if (rrow == 0) {
+  const int wr = wave * kRows16 + (lane >> 4);
+  if ((lane & 15) < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < EPV; ++c) s_o[wave][h][(j * LPR + sub) * EPV + c] = o[h][j * EPV + c];
-    if (lane == 0) {
+        for (int c = 0; c < EPV; c += 4)
+          s_o4[wr][h][((j * LPR + sub) * EPV + c) / 4] =
+              make_float4(o[h][j * EPV + c], o[h][j * EPV + c + 1], o[h][j * EPV + c + 2], o[h][j * EPV + c + 3]);
+    if ((lane & 15) == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s_m[wave][h] = m_run[h];
-        s_l[wave][h] = l_acc[h];
+        s_m[wr][h] = m_run[h];
+        s_l[wr][h] = l_acc[h];
       }
     }
   }
   __syncthreads();
-
-  for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) M = fmaxf(M, s_m[w][h]);
-    float acc = 0.f, lsum = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWavesPerGroup; ++w) {
-        const float sc = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - M);
-        acc = fmaf(sc, s_o[w][h][e], acc);
-        lsum = fmaf(sc, s_l[w][h], lsum);
-      }
+  if (threadIdx.x < G * kWave) {  // wave h: the common maximum and weights of head h
+    const int h = threadIdx.x / kWave, r = threadIdx.x % kWave;
+    const float mr = r < NWR ? s_m[r][h] : -INFINITY;
+    const float M = max_over<1, 32>(mr);
+    const float w = (r < NWR && mr != -INFINITY) ? fast_exp2(mr - M) : 0.f;
+    if (r < NWR) s_w[r][h] = w;
+    const float lw = sum_over<1, 32>(r < NWR ? w * s_l[r][h] : 0.f);
+    if (r == 0) {
+      s_M[h] = M;
+      s_Lw[h] = lw;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += kGroupThreads) {
+    const int h = idx / (D / 4), e4 = idx % (D / 4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int r = 0; r < NWR; ++r) {
+      const float w = s_w[r][h];
+      const float4 v = s_o4[r][h][e4];
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
     }
     const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
-    publish(P.part_o + row * D + e, acc);
-    if (e == 0) {
-      publish(P.part_ml + row * 2 + 0, M);
-      publish(P.part_ml + row * 2 + 1, lsum);
+    float* dst = P.part_o + row * D + e4 * 4;
+    publish(dst + 0, acc.x);
+    publish(dst + 1, acc.y);
+    publish(dst + 2, acc.z);
+    publish(dst + 3, acc.w);
+    if (e4 == 0) {
+      publish(P.part_ml + row * 2 + 0, s_M[h]);
+      publish(P.part_ml + row * 2 + 1, s_Lw[h]);
     }
   }
 
@@ -730,6 +796,7 @@ struct GateParams {
   const int64_t* focus_range;
   int32_t* call_list;
   int32_t* call_count;
+  int32_t* call_len;  // optional: committed length of each listed request
   int64_t* full_calls;
   int64_t* counters;
 };
@@ -790,6 +857,7 @@ __global__ __launch_bounds__(1024) void gate_kernel(GateParams P) {
     for (int w = 0; w < wave; ++w) before += s_wave_count[w];
     const uint64_t lower = lane == 0 ? 0ull : (ballot & ((1ull << lane) - 1ull));
     if (fire && P.call_list) P.call_list[before + __popcll(lower)] = b;
+    if (fire && P.call_len) P.call_len[before + __popcll(lower)] = t - 1;
     __syncthreads();
     if (threadIdx.x == 0) {
       int32_t total = 0;
@@ -1146,8 +1214,8 @@ int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stre
 }
 
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
-                int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
-                oda_stream s) {
+                int32_t* call_list, int32_t* call_count, int32_t* call_len, int64_t* full_calls,
+                int64_t* counters, oda_stream s) {
   if (batch <= 0) return 0;
   GateParams g{};
   g.batch = batch;
@@ -1169,6 +1237,7 @@ int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* sco
   g.focus_range = kv.focus_range;
   g.call_list = call_list;
   g.call_count = call_count;
+  g.call_len = call_len;
   g.full_calls = full_calls;
   g.counters = counters;
   const int threads = batch >= 1024 ? 1024 : ((batch + 63) / 64) * 64;
