@@ -43,7 +43,29 @@ def parse():
                     help="also time rho=0, rho=1 and always-Full for the savings check")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 8 times (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy() -> int:
+    """A plain copy kernel of known size: 1 GiB read and 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(8):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 8
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": 8, "us_per_launch": round(ms * 1e3, 2),
+                      "gbps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
 
 
 def kernel_sha() -> str:
@@ -53,6 +75,8 @@ def kernel_sha() -> str:
 
 def main() -> int:
     args = parse()
+    if args.calibrate_copy:
+        return calibrate_copy()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by request or KV head with no exchange; see the design notes)",
