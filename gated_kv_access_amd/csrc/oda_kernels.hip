@@ -308,113 +308,82 @@ __device__ void write_call_list(const AttnParams& P) {
 // merge of the split partials and the current token (run by one workgroup)
 
 constexpr int kMaxMergeSplits = 512;
+constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
-// Phase A loads every (m, l) of the `used` partials into LDS in one round and
-// computes the current token's score; phase B turns them into weights; phase C
-// spreads the partial-o reads over split lanes (16 loads in flight per thread)
-// and folds the lanes through LDS.
+// One thread per output element (h, e): it loads every partial (m, l, o[e])
+// of its head in rounds of kMergeBatch -- one round when used <= 32 -- and the
+// current token's score comes from a dot product across its wave (a wave's
+// outputs all belong to one head).  No LDS, no barrier.
 template <int DT, int D, int G>
 __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t used) {
   constexpr int ES = DT == ODA_BF16 ? 2 : 4;
   constexpr int EPT = D / kWave;
   constexpr int GD = G * D;
-  constexpr int SL = kGroupThreads / GD;  // split lanes per output
-  static_assert(SL >= 1 && SL * GD == kGroupThreads, "outputs must tile the workgroup");
-  __shared__ float s_cur[G], s_wcur[G], s_L[G];
-  __shared__ float s_m[G][kMaxMergeSplits];
-  __shared__ float s_l[G][kMaxMergeSplits];
-  __shared__ float s_red[SL][GD];
+  static_assert(GD <= kGroupThreads && GD % kWave == 0, "one thread per output, whole waves per head");
   const int tid = threadIdx.x;
+  if (tid >= GD) return;
   const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
+  const int h = tid / D, e = tid % D;
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
 
-  // A: this thread's first 16 partial outputs, the partial maxima and sums,
-  // and the current-token scores -- all loads issued before any is used.
-  const int o_idx = tid % GD, o_sl = tid / GD;
-  const int o_h = o_idx / D, o_e = o_idx % D;
-  const float* po = P.part_o + (head0 + o_h) * P.splits * D + o_e;
-  float x[16];
+  // current token: score (wave-wide dot product) and value element
+  const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * ES;
+  const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+  const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
+  float dot = 0.f;  // every wave of head h computes the same q.k_cur, EPT elements per lane
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int i = o_sl + u * SL;
-    x[u] = i < used ? collect(po + (int64_t)i * D) : 0.f;
-  }
-  for (int idx = tid; idx < G * used; idx += kGroupThreads) {
-    const int h = idx / used, i = idx % used;
-    const float* ml = P.part_ml + ((head0 + h) * P.splits + i) * 2;
-    s_m[h][i] = collect(ml);
-    s_l[h][i] = collect(ml + 1);
-  }
-  for (int h = wave; h < G; h += kWavesPerGroup) {
-    const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * ES;
-    const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-    float dot = 0.f;
-#pragma unroll
-    for (int c = 0; c < EPT; ++c) {
-      const int e = lane * EPT + c;
-      float qx, kx;
-      if constexpr (DT == ODA_BF16) {
-        qx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[e] << 16);
-        kx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[e] << 16);
-      } else {
-        qx = reinterpret_cast<const float*>(qrow)[e];
-        kx = reinterpret_cast<const float*>(krow)[e];
-      }
-      dot = fmaf(qx, kx, dot);
+  for (int c = 0; c < EPT; ++c) {
+    const int ee = lane * EPT + c;
+    float qx, kx;
+    if constexpr (DT == ODA_BF16) {
+      qx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[ee] << 16);
+      kx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[ee] << 16);
+    } else {
+      qx = reinterpret_cast<const float*>(qrow)[ee];
+      kx = reinterpret_cast<const float*>(krow)[ee];
     }
-    dot = sum_over<1, 32>(dot);
-    if (lane == 0) s_cur[h] = dot * P.scale_log2;
+    dot = fmaf(qx, kx, dot);
   }
-  __syncthreads();
+  float vx;
+  if constexpr (DT == ODA_BF16) vx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
+  else vx = reinterpret_cast<const float*>(vrow)[e];
 
-  // B: M = max over partials and the current token; weights exp2(m_i - M)
-  for (int h = wave; h < G; h += kWavesPerGroup) {
-    float mx = s_cur[h];
-    for (int i = lane; i < used; i += kWave) mx = fmaxf(mx, s_m[h][i]);
-    mx = max_over<1, 32>(mx);
-    float lsum = 0.f;
-    for (int i = lane; i < used; i += kWave) {
-      const float mi = s_m[h][i];
-      const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - mx);
-      s_m[h][i] = w;
-      lsum = fmaf(w, s_l[h][i], lsum);
-    }
-    lsum = sum_over<1, 32>(lsum);
-    if (lane == 0) {
-      const float wc = fast_exp2(s_cur[h] - mx);
-      s_wcur[h] = wc;
-      s_L[h] = lsum + wc;
-      s_cur[h] = mx;  // keep M for the lse
-    }
-  }
-  __syncthreads();
-
-  // C: weighted sum of the partial outputs
-  {
-    float acc = 0.f;
+  const float* ml = P.part_ml + (head0 + h) * P.splits * 2;
+  const float* po = P.part_o + (head0 + h) * P.splits * D + e;
+  float m[kMergeBatch], l[kMergeBatch], x[kMergeBatch];
+  const int n0 = used < kMergeBatch ? used : kMergeBatch;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = o_sl + u * SL;
-      if (i < used) acc = fmaf(s_m[o_h][i], x[u], acc);
+  for (int i = 0; i < kMergeBatch; ++i) {
+    if (i < n0) {
+      m[i] = collect(ml + 2 * i);
+      l[i] = collect(ml + 2 * i + 1);
+      x[i] = collect(po + (int64_t)i * D);
     }
-    for (int i = o_sl + 16 * SL; i < used; i += SL) acc = fmaf(s_m[o_h][i], collect(po + (int64_t)i * D), acc);
-    s_red[o_sl][o_idx] = acc;
   }
-  __syncthreads();
-  if (tid < GD) {
-    const int h = tid / D, e = tid % D;
-    float acc = 0.f;
+  const float s_cur = sum_over<1, 32>(dot) * P.scale_log2;
+  float M = s_cur;
 #pragma unroll
-    for (int sl = 0; sl < SL; ++sl) acc += s_red[sl][tid];
-    const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-    float vx;
-    if constexpr (DT == ODA_BF16) vx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
-    else vx = reinterpret_cast<const float*>(vrow)[e];
-    acc = fmaf(s_wcur[h], vx, acc);
-    P.out[(head0 + h) * D + e] = acc / s_L[h];
+  for (int i = 0; i < kMergeBatch; ++i)
+    if (i < n0) M = fmaxf(M, m[i]);
+  for (int i = kMergeBatch; i < used; ++i) M = fmaxf(M, collect(ml + 2 * i));
+  const float wc = fast_exp2(s_cur - M);
+  float L = wc, acc = wc * vx;
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; ++i) {
+    if (i < n0) {
+      const float w = m[i] == -INFINITY ? 0.f : fast_exp2(m[i] - M);
+      L = fmaf(w, l[i], L);
+      acc = fmaf(w, x[i], acc);
+    }
   }
-  if (P.lse != nullptr && tid < G) P.lse[head0 + tid] = (s_cur[tid] + __log2f(s_L[tid])) * kLn2;
+  for (int i = kMergeBatch; i < used; ++i) {
+    const float mi = collect(ml + 2 * i);
+    const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+    L = fmaf(w, collect(ml + 2 * i + 1), L);
+    acc = fmaf(w, collect(po + (int64_t)i * D), acc);
+  }
+  P.out[(head0 + h) * D + e] = acc / L;
+  if (P.lse != nullptr && e == 0) P.lse[head0 + h] = (M + __log2f(L)) * kLn2;
 }
 
 // ----------------------------------------------------------------------------
@@ -700,14 +669,13 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
 
   // Epilogue 2: the first LPR lanes of each 16-lane row hold distinct element
-  // slices; they store the row's sums, and the 8 waves x 4 rows are folded
-  // through LDS into this workgroup's partial, published device-wide.
+  // slices; they store the row's sums, and after one barrier each output
+  // thread folds the 8 waves x 4 rows itself (weights computed in place) and
+  // publishes this workgroup's partial device-wide.
   constexpr int NWR = kWavesPerGroup * kRows16;
-  __shared__ float4 s_o4[NWR][G][D / 4];
+  __shared__ float s_o[NWR][G][D];
   __shared__ float s_m[NWR][G];
   __shared__ float s_l[NWR][G];
-  __shared__ float s_w[NWR][G];
-  __shared__ float s_M[G], s_Lw[G];
   __shared__ int32_t s_last;
   const int wr = wave * kRows16 + (lane >> 4);
   if ((lane & 15) < LPR) {
@@ -717,7 +685,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int c = 0; c < EPV; c += 4)
-          s_o4[wr][h][((j * LPR + sub) * EPV + c) / 4] =
+          *reinterpret_cast<float4*>(&s_o[wr][h][(j * LPR + sub) * EPV + c]) =
               make_float4(o[h][j * EPV + c], o[h][j * EPV + c + 1], o[h][j * EPV + c + 2], o[h][j * EPV + c + 3]);
     if ((lane & 15) == 0) {
 #pragma unroll
@@ -728,40 +696,24 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
   }
   __syncthreads();
-  if (threadIdx.x < G * kWave) {  // wave h: the common maximum and weights of head h
-    const int h = threadIdx.x / kWave, r = threadIdx.x % kWave;
-    const float mr = r < NWR ? s_m[r][h] : -INFINITY;
-    const float M = max_over<1, 32>(mr);
-    const float w = (r < NWR && mr != -INFINITY) ? fast_exp2(mr - M) : 0.f;
-    if (r < NWR) s_w[r][h] = w;
-    const float lw = sum_over<1, 32>(r < NWR ? w * s_l[r][h] : 0.f);
-    if (r == 0) {
-      s_M[h] = M;
-      s_Lw[h] = lw;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += kGroupThreads) {
-    const int h = idx / (D / 4), e4 = idx % (D / 4);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
+    const int h = idx / D, e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < NWR; ++r) M = fmaxf(M, s_m[r][h]);
+    float acc = 0.f, lsum = 0.f;
 #pragma unroll 8
     for (int r = 0; r < NWR; ++r) {
-      const float w = s_w[r][h];
-      const float4 v = s_o4[r][h][e4];
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+      const float mr = s_m[r][h];
+      const float w = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
+      acc = fmaf(w, s_o[r][h][e], acc);
+      lsum = fmaf(w, s_l[r][h], lsum);
     }
     const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
-    float* dst = P.part_o + row * D + e4 * 4;
-    publish(dst + 0, acc.x);
-    publish(dst + 1, acc.y);
-    publish(dst + 2, acc.z);
-    publish(dst + 3, acc.w);
-    if (e4 == 0) {
-      publish(P.part_ml + row * 2 + 0, s_M[h]);
-      publish(P.part_ml + row * 2 + 1, s_Lw[h]);
+    publish(P.part_o + row * D + e, acc);
+    if (e == 0) {
+      publish(P.part_ml + row * 2 + 0, M);
+      publish(P.part_ml + row * 2 + 1, lsum);
     }
   }
 
