@@ -27,7 +27,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboda_oracle.so")
 
-BF16, F32 = 0, 1
+BF16, F32, FP8 = 0, 1, 2
 GATED, SLIDING = 0, 1
 LOCAL, FULL = 0, 1
 ACCT_FIELDS = ("steps", "full_calls", "f_local", "f_full_taken", "f_full_always",
@@ -42,6 +42,7 @@ class _Cfg(ctypes.Structure):
         ("sw_window", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("focus", ctypes.c_int32), ("pad_", ctypes.c_int32),
         ("scale", ctypes.c_double), ("recall_flops", ctypes.c_int64),
+        ("k_scale", ctypes.c_double), ("v_scale", ctypes.c_double),
         ("layer_kind", ctypes.c_void_p),
     ]
 
@@ -60,6 +61,8 @@ class OracleConfig:
     scale: float = 0.0
     recall_flops: int = 0
     layer_kind: Optional[Sequence[int]] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     _kinds: Optional[np.ndarray] = field(default=None, repr=False)
 
     def to_c(self) -> _Cfg:
@@ -69,6 +72,7 @@ class OracleConfig:
         c.sink, c.window, c.sw_window = self.sink, self.window, self.sw_window
         c.dtype, c.focus, c.pad_ = self.dtype, int(bool(self.focus)), 0
         c.scale, c.recall_flops = float(self.scale), int(self.recall_flops)
+        c.k_scale, c.v_scale = float(self.k_scale), float(self.v_scale)
         if self.layer_kind is not None:
             self._kinds = np.ascontiguousarray(np.asarray(self.layer_kind, dtype=np.uint8))
             assert self._kinds.shape == (self.num_layers,)
@@ -91,7 +95,10 @@ def _bind(path: str):
                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
     L.oracle_access_set.restype = ctypes.c_int64
     L.oracle_attention.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_int32, ctypes.c_double, P, ctypes.c_int64, P, P]
+                                   ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double, P,
+                                   ctypes.c_int64, P, P]
+    L.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+    L.oracle_fp8_e4m3.restype = ctypes.c_double
     L.oracle_attention.restype = ctypes.c_double
     L.oracle_gate.argtypes = [ctypes.c_float, ctypes.c_float]
     L.oracle_gate.restype = ctypes.c_int
@@ -137,8 +144,9 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def _raw(a: np.ndarray, dtype: int) -> np.ndarray:
-    """Input arrays travel as raw element words: uint16 for bf16, float32 for f32."""
-    want = np.uint16 if dtype == BF16 else np.float32
+    """Input arrays travel as raw element words: uint16 for bf16, float32 for f32,
+    uint8 for FP8 E4M3."""
+    want = {BF16: np.uint16, F32: np.float32, FP8: np.uint8}[dtype]
     if a.dtype != want:
         raise TypeError(f"expected {want} array for dtype {dtype}, got {a.dtype}")
     return np.ascontiguousarray(a)
@@ -168,20 +176,28 @@ def gate(score: float, theta: float = 0.0) -> bool:
     return bool(lib().oracle_gate(score, theta))
 
 
+def _qtype(dtype: int) -> int:
+    return BF16 if dtype == FP8 else dtype
+
+
+def fp8_e4m3(code: int) -> float:
+    return float(lib().oracle_fp8_e4m3(int(code)))
+
+
 def attention(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, g: int, positions: np.ndarray,
-              dtype: int, scale: float = 0.0):
+              dtype: int, scale: float = 0.0, k_scale: float = 1.0, v_scale: float = 1.0):
     """One query head over one request's sequence rows.
 
-    q: [d]; kseq, vseq: [T][Hkv][d] raw words; positions: 1-based int64.
-    Returns (out[d] float64, lse float)."""
-    q, kseq, vseq = _raw(q, dtype), _raw(kseq, dtype), _raw(vseq, dtype)
+    q: [d] (bf16 words when K/V are FP8); kseq, vseq: [T][Hkv][d] raw words;
+    positions: 1-based int64.  Returns (out[d] float64, lse float)."""
+    q, kseq, vseq = _raw(q, _qtype(dtype)), _raw(kseq, dtype), _raw(vseq, dtype)
     T, Hkv, d = kseq.shape
     pos = np.ascontiguousarray(positions, dtype=np.int64)
     assert pos.size == 0 or (pos.min() >= 1 and pos.max() <= T)
     out = np.zeros(d, dtype=np.float64)
     z = np.zeros(max(pos.size, 1), dtype=np.float64)
     sc = scale if scale > 0 else 1.0 / np.sqrt(d)
-    lse = lib().oracle_attention(_ptr(q), _ptr(kseq), _ptr(vseq), Hkv, d, g, dtype, sc,
+    lse = lib().oracle_attention(_ptr(q), _ptr(kseq), _ptr(vseq), Hkv, d, g, dtype, sc, k_scale, v_scale,
                                  _ptr(pos), pos.size, _ptr(out), _ptr(z))
     return out, float(lse)
 
@@ -202,8 +218,8 @@ def decode_run(cfg: OracleConfig, prefill: Sequence[int], kseq: np.ndarray, vseq
     kseq, vseq: [L][B][T][Hkv][d] raw words holding every position of the run;
     q_local (and q_full): [K][L][B][Hq][d]; score: [K][B] float32."""
     kseq, vseq = _raw(kseq, cfg.dtype), _raw(vseq, cfg.dtype)
-    q_local = _raw(q_local, cfg.dtype)
-    q_full = None if q_full is None else _raw(q_full, cfg.dtype)
+    q_local = _raw(q_local, _qtype(cfg.dtype))
+    q_full = None if q_full is None else _raw(q_full, _qtype(cfg.dtype))
     L, B, T, Hkv, d = kseq.shape
     K = q_local.shape[0]
     Hq = cfg.num_q_heads

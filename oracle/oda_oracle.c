@@ -20,7 +20,12 @@
  * one contiguous region of the cache; sliding-window layers keep a fixed
  * recent window in both access modes.
  *
- * Arithmetic: every value (bf16 or fp32 input) is widened exactly to double;
+ * FP8 KV: quantising the stored cache is the complementary technique of the
+ * kongchang.com page, section "The KV Cache Compression Technology Ecosystem".
+ * K/V may be FP8 E4M3 codes (the OCP OFP8 encoding) with one dequantisation
+ * scale per tensor; the queries stay bf16.
+ *
+ * Arithmetic: every value (bf16, fp32 or E4M3 input) is widened exactly to double;
  * dot products, exp and log are plain fp64 libm calls.  Attention is the
  * textbook softmax: z_p = scale * <q, K_p>, m = max z, Z = sum exp(z - m),
  * O = sum (exp(z_p - m)/Z) V_p, lse = m + log Z.  No splitting, blocking or
@@ -29,7 +34,7 @@
  *
  * Parity-pinned by tests/test_oracle_pins.py (brute-force sets, closed forms,
  * torch scaled_dot_product_attention in float64, special cases, hand-worked
- * fixtures in tests/golden/).
+ * fixtures in tests/golden/, the E4M3 code table against torch.float8_e4m3fn).
  */
 #include <math.h>
 #include <stdint.h>
@@ -39,7 +44,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_BF16 = 0, OR_F32 = 1 };
+enum { OR_BF16 = 0, OR_F32 = 1, OR_FP8 = 2 };
 enum { OR_GATED = 0, OR_SLIDING = 1 };
 enum { OR_LOCAL = 0, OR_FULL = 1 };
 enum { OR_ACCT_STEPS = 0, OR_ACCT_FULL_CALLS, OR_ACCT_F_LOCAL, OR_ACCT_F_FULL_TAKEN,
@@ -50,24 +55,43 @@ typedef struct {
   int32_t num_layers, num_q_heads, num_kv_heads, head_dim;
   int32_t sink, window;        /* s, w of gated layers                          */
   int32_t sw_window;           /* window of sliding-window layers (no sinks)     */
-  int32_t dtype;               /* OR_BF16 (raw 16-bit words) or OR_F32           */
+  int32_t dtype;               /* K/V: OR_BF16 (16-bit words), OR_F32, or OR_FP8
+                                  (e4m3 bytes; queries are then bf16 words)      */
   int32_t focus;               /* 0: a fired gated layer reads S^F_t;
                                   1: it reads S^L_t U [a, b)                     */
   int32_t pad_;
   double  scale;               /* softmax scale; 0 means 1/sqrt(head_dim)        */
   int64_t recall_flops;        /* F_Recall charged per request per step          */
+  double  k_scale, v_scale;    /* dequantisation: K = k_scale * code value, V likewise;
+                                  0 means 1                                       */
   const uint8_t* layer_kind;   /* [num_layers], OR_GATED / OR_SLIDING; NULL: all gated */
 } oracle_cfg;
 
+/* FP8 E4M3 (the "fn" variant: no infinities): sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits.  Exponent field 0 holds subnormals m/8 * 2^-6;
+ * exponent 15 with mantissa 7 is NaN; every other code is (1 + m/8) * 2^(e-7). */
+double oracle_fp8_e4m3(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
 static double widen(const void* base, int32_t dtype, int64_t idx) {
   if (dtype == OR_F32) return (double)((const float*)base)[idx];
+  if (dtype == OR_FP8) return oracle_fp8_e4m3(((const uint8_t*)base)[idx]);
   uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
   return (double)f;
 }
 
-static int64_t esize(int32_t dtype) { return dtype == OR_F32 ? 4 : 2; }
+/* Queries are bf16 when K/V are FP8. */
+static int32_t q_dtype(int32_t dtype) { return dtype == OR_FP8 ? OR_BF16 : dtype; }
+
+static int64_t esize(int32_t dtype) { return dtype == OR_F32 ? 4 : (dtype == OR_FP8 ? 1 : 2); }
 
 static int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 static int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
@@ -115,14 +139,15 @@ int64_t oracle_access_set(const oracle_cfg* c, int32_t kind, int32_t mode, int64
  *   z   : caller scratch of n doubles
  * Writes out[head_dim] and returns lse = m + log Z. */
 double oracle_attention(const void* q, const void* kv_k, const void* kv_v, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t g, int32_t dtype, double scale,
-                        const int64_t* pos, int64_t n, double* out, double* z) {
+                        int32_t head_dim, int32_t g, int32_t dtype, double scale, double k_scale,
+                        double v_scale, const int64_t* pos, int64_t n, double* out, double* z) {
   const int64_t d = head_dim;
+  const int32_t qt = q_dtype(dtype);
   double m = -INFINITY;
   for (int64_t i = 0; i < n; ++i) {
     const int64_t row = ((pos[i] - 1) * num_kv_heads + g) * d;
     double dot = 0.0;
-    for (int64_t j = 0; j < d; ++j) dot += widen(q, dtype, j) * widen(kv_k, dtype, row + j);
+    for (int64_t j = 0; j < d; ++j) dot += widen(q, qt, j) * (k_scale * widen(kv_k, dtype, row + j));
     z[i] = scale * dot;
     if (z[i] > m) m = z[i];
   }
@@ -132,7 +157,7 @@ double oracle_attention(const void* q, const void* kv_k, const void* kv_v, int32
   for (int64_t i = 0; i < n; ++i) {
     const double wgt = exp(z[i] - m) / Z;
     const int64_t row = ((pos[i] - 1) * num_kv_heads + g) * d;
-    for (int64_t j = 0; j < d; ++j) out[j] += wgt * widen(kv_v, dtype, row + j);
+    for (int64_t j = 0; j < d; ++j) out[j] += wgt * (v_scale * widen(kv_v, dtype, row + j));
   }
   return m + log(Z);
 }
@@ -182,7 +207,8 @@ void oracle_step_accounting(const oracle_cfg* c, int64_t t, int32_t fired, int64
  * position becoming visible to later steps.
  *
  *   kseq, vseq : [L][B][T][Hkv][d]   (T rows per request; rows >= prefill_b + K unused)
- *   q_local    : [K][L][B][Hq][d];   q_full: same shape, NULL = reuse q_local
+ *   q_local    : [K][L][B][Hq][d] (bf16 words when K/V are FP8); q_full: same shape,
+ *                NULL = reuse q_local
  *   score      : [K][B] fp32;        focus: [B][2] (a, b) or NULL
  *   active     : [B] or NULL (all active); inactive requests are skipped
  * Outputs (any may be NULL except out):
@@ -201,8 +227,9 @@ int oracle_decode_run(const oracle_cfg* c, int32_t B, int32_t K, const int64_t* 
   for (int32_t b = 0; b < B; ++b)
     if (prefill[b] < 0 || prefill[b] + K > T) return -1;
   const double scale = c->scale > 0.0 ? c->scale : 1.0 / sqrt((double)d);
+  const double ks = c->k_scale > 0.0 ? c->k_scale : 1.0, vs = c->v_scale > 0.0 ? c->v_scale : 1.0;
   const int32_t group = Hq / Hkv;
-  const int64_t es = esize(c->dtype);
+  const int64_t es = esize(c->dtype), qes = esize(q_dtype(c->dtype));
   const int64_t seq_stride = T * Hkv * d;  /* elements per (layer, request) sequence */
   const void* qf_base = q_full ? q_full : q_local;
   uint8_t* fired = (uint8_t*)calloc((size_t)(B > 0 ? B : 1), 1);
@@ -242,15 +269,15 @@ int oracle_decode_run(const oracle_cfg* c, int32_t B, int32_t K, const int64_t* 
           const int64_t ooff = qoff;
           const int64_t loff = (((int64_t)(k - 1) * L + l) * B + b) * Hq + h;
           const int32_t mode = fired[b] ? OR_FULL : OR_LOCAL;
-          const void* qb = (const char*)(fired[b] ? qf_base : q_local) + qoff * es;
+          const void* qb = (const char*)(fired[b] ? qf_base : q_local) + qoff * qes;
           /* The Local attempt is always computed; a fired request then
            * recomputes over its Full set and that result is the one kept. */
           const int64_t nl = oracle_access_set(c, kind, OR_LOCAL, t, fa, fb, pos);
-          double l_lse = oracle_attention((const char*)q_local + qoff * es, kb, vb, Hkv, d,
-                                          h / group, c->dtype, scale, pos, nl, out + ooff, z);
+          double l_lse = oracle_attention((const char*)q_local + qoff * qes, kb, vb, Hkv, d,
+                                          h / group, c->dtype, scale, ks, vs, pos, nl, out + ooff, z);
           if (mode == OR_FULL) {
             const int64_t nf = oracle_access_set(c, kind, OR_FULL, t, fa, fb, pos);
-            l_lse = oracle_attention(qb, kb, vb, Hkv, d, h / group, c->dtype, scale, pos, nf,
+            l_lse = oracle_attention(qb, kb, vb, Hkv, d, h / group, c->dtype, scale, ks, vs, pos, nf,
                                      out + ooff, z);
           }
           if (lse) lse[loff] = l_lse;

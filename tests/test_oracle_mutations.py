@@ -13,7 +13,7 @@ SRC = os.path.join(os.path.dirname(orc.__file__), "oda_oracle.c")
 
 # (name, original text, mutated text, pin functions expected to catch it)
 MUTATIONS = [
-    ("gqa_modulo", "h / group, c->dtype, scale, pos, nl", "h % Hkv, c->dtype, scale, pos, nl",
+    ("gqa_modulo", "h / group, c->dtype, scale, ks, vs, pos, nl", "h % Hkv, c->dtype, scale, ks, vs, pos, nl",
      ["test_run_gqa_head_grouping"]),
     ("window_off_by_one", "p >= max64(1, t - c->window + 1)", "p >= max64(1, t - c->window)",
      ["worked_local"]),
@@ -30,6 +30,16 @@ MUTATIONS = [
     ("value_row_from_query_head", "const int64_t row = ((pos[i] - 1) * num_kv_heads + g) * d;\n    for (int64_t j = 0; j < d; ++j) out[j]",
      "const int64_t row = ((pos[i] - 1) * num_kv_heads) * d;\n    for (int64_t j = 0; j < d; ++j) out[j]",
      ["test_attention_matches_torch_sdpa_float64"]),
+    ("fp8_bias_8", "else v = ldexp(1.0 + (double)m / 8.0, e - 7);", "else v = ldexp(1.0 + (double)m / 8.0, e - 8);",
+     ["worked_fp8"]),
+    ("fp8_subnormal_exponent", "if (e == 0) v = ldexp((double)m / 8.0, -6);", "if (e == 0) v = ldexp((double)m / 8.0, -7);",
+     ["worked_fp8"]),
+    ("fp8_no_nan", "if (e == 15 && m == 7) return NAN;", "if (e == 16 && m == 7) return NAN;", ["worked_fp8"]),
+    ("fp8_k_scale_dropped", "(k_scale * widen(kv_k, dtype, row + j))", "(widen(kv_k, dtype, row + j))",
+     ["fp8_sdpa"]),
+    ("fp8_v_scale_dropped", "(v_scale * widen(kv_v, dtype, row + j))", "(widen(kv_v, dtype, row + j))",
+     ["fp8_sdpa"]),
+    ("fp8_query_read_as_fp8", "const int32_t qt = q_dtype(dtype);", "const int32_t qt = dtype;", ["fp8_sdpa"]),
 ]
 
 
@@ -47,6 +57,11 @@ def _run_pin(name):
     elif name == "worked_accounting":
         for case in g("accounting.json")["cases"]:
             pins.test_accounting_worked_examples(case)
+    elif name == "worked_fp8":
+        for case in g("fp8_e4m3.json")["codes"]:
+            pins.test_fp8_e4m3_worked_codes(case)
+    elif name == "fp8_sdpa":
+        pins.test_fp8_attention_matches_torch_sdpa_on_dequantised_values(64)
     elif name == "test_attention_matches_torch_sdpa_float64":
         for dt in (orc.F32, orc.BF16):
             pins.test_attention_matches_torch_sdpa_float64(dt, 64)

@@ -145,6 +145,78 @@ def test_attention_matches_torch_sdpa_float64(dtype, d):
                 assert abs(lse - torch.logsumexp(z, 0).item()) < 1e-12
 
 
+# --------------------------------------------------------------------------- FP8 E4M3 KV
+
+@pytest.mark.parametrize("case", _load("fp8_e4m3.json")["codes"], ids=lambda c: c["code"])
+def test_fp8_e4m3_worked_codes(case):
+    got = orc.fp8_e4m3(int(case["code"], 16))
+    if case["value"] == "nan":
+        assert math.isnan(got)
+    else:
+        assert got == case["value"] and math.copysign(1.0, got) == math.copysign(1.0, case["value"])
+
+
+def test_fp8_e4m3_all_codes_match_torch_float8_e4m3fn():
+    """Library cross-check over the whole code space: torch's float8_e4m3fn
+    decoding of each byte, widened to float64."""
+    want = torch.arange(256, dtype=torch.int16).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.fp8_e4m3(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_attention_matches_torch_sdpa_on_dequantised_values(d):
+    """FP8 K/V with per-tensor scales: the oracle equals float64 SDPA over
+    k_scale * decode(K) and v_scale * decode(V), with bf16 queries."""
+    g = torch.Generator().manual_seed(99 + d)
+    T, Hkv = 500, 2
+    k_scale, v_scale = 0.0625, 3.0
+    K8 = (torch.randn(T, Hkv, d, generator=g) * 4).to(torch.float8_e4m3fn)
+    V8 = (torch.randn(T, Hkv, d, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    q = torch.randn(d, generator=g) * 2.0
+    qw = q.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    kw, vw = K8.view(torch.uint8).numpy(), V8.view(torch.uint8).numpy()
+    cfg = _cfg(sink=4, window=64)
+    for t in (3, 68, 500):
+        for mode in (orc.LOCAL, orc.FULL):
+            pos = orc.access_set(cfg, orc.GATED, mode, t)
+            idx = torch.from_numpy(pos - 1)
+            for kvh in range(Hkv):
+                out, lse = orc.attention(qw, kw, vw, kvh, pos, orc.FP8, k_scale=k_scale, v_scale=v_scale)
+                k64 = K8.to(torch.float64)[idx, kvh] * k_scale
+                v64 = V8.to(torch.float64)[idx, kvh] * v_scale
+                q64 = q.to(torch.bfloat16).to(torch.float64)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    q64.view(1, 1, 1, d), k64.view(1, 1, -1, d), v64.view(1, 1, -1, d))
+                np.testing.assert_allclose(out, ref.view(d).numpy(), atol=1e-12, rtol=0)
+                z = (k64 @ q64) / math.sqrt(d)
+                assert abs(lse - torch.logsumexp(z, 0).item()) < 1e-12
+
+
+def test_fp8_run_equals_bf16_run_on_exactly_representable_values():
+    """Every E4M3 value is exact in bf16, so a decode run over FP8 codes with
+    unit scales equals the same run over the bf16 words of the decoded values."""
+    L, B, Hq, Hkv, d, P, K = 1, 2, 2, 1, 64, 90, 6
+    T = P + K
+    g = torch.Generator().manual_seed(7)
+    k8 = torch.randn(L, B, T, Hkv, d, generator=g).to(torch.float8_e4m3fn)
+    v8 = torch.randn(L, B, T, Hkv, d, generator=g).to(torch.float8_e4m3fn)
+    q = torch.randn(K, L, B, Hq, d, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    score = np.where(np.arange(K * B).reshape(K, B) % 3 == 0, 1.0, -1.0).astype(np.float32)
+    prefill = np.full(B, P, np.int64)
+    base = dict(num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, sink=4, window=32)
+    r8 = orc.decode_run(orc.OracleConfig(dtype=orc.FP8, **base), prefill, k8.view(torch.uint8).numpy(),
+                        v8.view(torch.uint8).numpy(), q, score)
+    kb = k8.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vb = v8.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rb = orc.decode_run(orc.OracleConfig(dtype=orc.BF16, **base), prefill, kb, vb, q, score)
+    np.testing.assert_array_equal(r8["out"], rb["out"])
+    np.testing.assert_array_equal(r8["lse"], rb["lse"])
+
+
 def test_attention_special_cases():
     rng = np.random.default_rng(5)
     d, T = 64, 300
