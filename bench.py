@@ -1,6 +1,7 @@
 """Decode-step throughput of the ODA hot path on one MI355X.
 
-Workload (default): 28 layers, 16 query / 8 KV heads of 128, bf16 K/V,
+Workload (default): 28 layers, 16 query / 8 KV heads of 128, bf16 K/V
+(--kv-dtype fp8: E4M3 K/V codes with per-tensor scales, bf16 queries),
 batch 1, 131072-token prefilled context, s = 4, w = 2048, paged blocks of 16,
 recall scores drawn so exactly 12.5% of the timed steps fire.  One step is
 the whole hot path -- Local pass of every layer, device gate, gated Full pass
@@ -24,7 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_attention_ctx128k.json")
+TRAFFIC_FILE = {"bf16": os.path.join(ROOT, "profiles", "traffic_full_attention_ctx128k.json"),
+                "fp8": os.path.join(ROOT, "profiles", "traffic_full_attention_ctx128k_fp8.json")}
+DTYPE_LABEL = {"bf16": "bf16", "fp8": "fp8_e4m3 K/V, bf16 q"}
 KERNEL_SRC = os.path.join(ROOT, "gated_kv_access_amd", "csrc", "oda_kernels.hip")
 
 
@@ -38,6 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--rho", type=float, default=None, help="override the Full-call rate")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="KV cache storage: bf16, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--roofline-launches", type=int, default=56)
     ap.add_argument("--sweep", action="store_true",
                     help="also time rho=0, rho=1 and always-Full for the savings check")
@@ -92,7 +97,7 @@ def main() -> int:
 
     B.load()
     K, Wm = args.steps, args.warmup
-    base = W.config(2)
+    base = W.config(2) if args.kv_dtype == "bf16" else W.config(2).fp8()
     rho = base.rho[0] if args.rho is None else args.rho
     wl = base.with_(steps=Wm + K, rho=(rho,))
     log(f"workload {wl.name}: prefill {wl.prefill[0]}, warmup {Wm}, timed {K}, rho {rho}")
@@ -154,14 +159,14 @@ def main() -> int:
     bytes_per_launch = (t_now - 1) * Hkv * d * 2 * wl.esize  # K and V rows streamed from the paged cache
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as fh:
+    if os.path.exists(TRAFFIC_FILE[args.kv_dtype]):
+        with open(TRAFFIC_FILE[args.kv_dtype]) as fh:
             tr = json.load(fh)
         if tr.get("kernel_sha") == kernel_sha():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "attention_kernel<bf16,128,G2,paged,ballot>", "avg_launch_us": round(avg_us, 2),
+                "kernel": f"attention_kernel<{args.kv_dtype},128,G2,paged,ballot>", "avg_launch_us": round(avg_us, 2),
                 "bytes_per_launch": bytes_per_launch, "launches": R}
     log(f"roofline: Full-pass kernel {avg_us:.1f} us/launch, {achieved:.0f} GB/s = "
         f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak")
@@ -186,11 +191,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_LABEL[args.kv_dtype],
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "q_heads": wl.num_q_heads, "kv_heads": Hkv,
                    "head_dim": d, "batch": wl.batch, "prefill": wl.prefill[0], "sink": wl.sink,
-                   "window": wl.window, "block_size": wl.block_size, "rho": rho,
+                   "window": wl.window, "block_size": wl.block_size, "rho": rho, "kv_dtype": wl.dtype,
                    "full_calls_timed": int(f["full_calls"]), "parallelism": "single GPU"},
         "tokens_per_s": round(steps_per_s * wl.batch, 2),
         "effective_kv_gbps": round(kv_gbps, 1),
@@ -282,14 +287,18 @@ def cpu_baseline(st, wl, q, rho, n_layers, log):
     P0 = t_end - k
     layers = list(range(n_layers))
     rows = t_end
-    ks = np.zeros((n_layers, 1, rows, wl.num_kv_heads, wl.head_dim), np.uint16)
+    fp8 = wl.dtype == "fp8"
+    kv_words = (lambda x: x.view(torch.uint8).cpu().numpy()) if fp8 else \
+        (lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16))
+    ks = np.zeros((n_layers, 1, rows, wl.num_kv_heads, wl.head_dim), np.uint8 if fp8 else np.uint16)
     vs = np.zeros_like(ks)
     for i, l in enumerate(layers):
-        ks[i, 0] = W.gen_sequence(wl, l, 0, "k", "cuda")[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
-        vs[i, 0] = W.gen_sequence(wl, l, 0, "v", "cuda")[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        ks[i, 0] = kv_words(W.gen_sequence(wl, l, 0, "k", "cuda")[:rows])
+        vs[i, 0] = kv_words(W.gen_sequence(wl, l, 0, "v", "cuda")[:rows])
     qq = q[:k, :n_layers].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     cfg = orc.OracleConfig(n_layers, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, sink=wl.sink,
-                           window=wl.window, dtype=orc.BF16)
+                           window=wl.window, dtype=orc.FP8 if fp8 else orc.BF16,
+                           k_scale=wl.k_scale, v_scale=wl.v_scale)
     threads = orc.get_threads()
     times = {}
     for label, val in (("local", -1.0), ("full", 1.0)):

@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liboda.so")
 
-BF16, F32 = 0, 1
+BF16, F32, FP8_E4M3 = 0, 1, 2
 LAYER_GATED, LAYER_SLIDING = 0, 1
 ACCT_FIELDS = ("steps", "full_calls", "f_local", "f_full_taken", "f_full_always",
                "delta_f", "kv_bytes", "f_recall")
@@ -44,6 +44,7 @@ class OdaDims(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("focus", ctypes.c_int32), ("full_splits", ctypes.c_int32),
         ("local_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("reserved0", ctypes.c_int32), ("recall_flops", ctypes.c_int64),
         ("layer_kind", ctypes.c_void_p),
     ]

@@ -33,10 +33,12 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
   if (d->num_layers < 1 || d->num_layers > ODA_MAX_LAYERS) return ODA_ERR_INVALID_ARG;
   if (d->num_q_heads < 1 || d->num_kv_heads < 1) return ODA_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return ODA_ERR_INVALID_ARG;
-  if (d->head_dim < 1 || d->kv_dtype < 0 || d->kv_dtype > 1) return ODA_ERR_INVALID_ARG;
+  if (d->head_dim < 1 || d->kv_dtype < ODA_BF16 || d->kv_dtype > ODA_FP8_E4M3) return ODA_ERR_INVALID_ARG;
   if (d->sink < 0 || d->max_batch < 1 || d->max_batch > ODA_MAX_BATCH) return ODA_ERR_INVALID_ARG;
   if (d->full_splits < 0 || d->local_splits < 0 || d->reserved0 != 0) return ODA_ERR_INVALID_ARG;
   if (!(d->softmax_scale >= 0.f) || isinf(d->softmax_scale)) return ODA_ERR_INVALID_ARG;
+  if (!(d->k_scale >= 0.f) || isinf(d->k_scale) || !(d->v_scale >= 0.f) || isinf(d->v_scale))
+    return ODA_ERR_INVALID_ARG;
   if (d->recall_flops < 0 || (d->focus != 0 && d->focus != 1)) return ODA_ERR_INVALID_ARG;
   p->L = d->num_layers;
   p->Hq = d->num_q_heads;
@@ -44,7 +46,8 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
   p->D = d->head_dim;
   p->G = d->num_q_heads / d->num_kv_heads;
   p->dtype = d->kv_dtype;
-  p->esize = d->kv_dtype == ODA_BF16 ? 2 : 4;
+  p->esize = d->kv_dtype == ODA_F32 ? 4 : (d->kv_dtype == ODA_BF16 ? 2 : 1);
+  p->q_esize = d->kv_dtype == ODA_F32 ? 4 : 2;
   p->sink = d->sink;
   p->window = d->window;
   p->sw_window = d->sw_window;
@@ -76,7 +79,9 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
   if (p->Lg > 0)
     while ((1 << p->block_shift) < p->block_size) ++p->block_shift;
   const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)p->D);
-  p->scale_log2 = scale * 1.44269504088896340736f;
+  const float k_scale = d->k_scale > 0.f ? d->k_scale : 1.f;
+  p->scale_log2 = scale * k_scale * 1.44269504088896340736f;
+  p->v_scale = d->v_scale > 0.f ? d->v_scale : 1.f;
   p->tile_rows = oda::tile_rows_for(p->dtype, p->D);
   return ODA_OK;
 }
@@ -236,6 +241,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
+  a.v_scale = p.v_scale;
   return hip_status(oda::launch_attention(p, a, batch, s));
 }
 
@@ -352,7 +358,7 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   if (st != ODA_OK) return st;
   if (batch == 0) return ODA_OK;
   const Plan& p = c.plan;
-  const int64_t q_layer = (int64_t)batch * p.Hq * p.D * p.esize;
+  const int64_t q_layer = (int64_t)batch * p.Hq * p.D * p.q_esize;
   const int64_t kv_layer = (int64_t)batch * p.Hkv * p.D * p.esize;
   const int64_t o_layer = (int64_t)batch * p.Hq * p.D;
   const int64_t l_layer = (int64_t)batch * p.Hq;

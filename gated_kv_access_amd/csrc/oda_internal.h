@@ -20,7 +20,7 @@ enum Source : int32_t { kSrcRing = 0, kSrcPaged = 1 };
 
 // Everything the host derives once from oda_dims.
 struct Plan {
-  int32_t L, Hq, Hkv, D, G, dtype, esize;
+  int32_t L, Hq, Hkv, D, G, dtype, esize, q_esize;  // esize: K/V bytes; q_esize: query bytes
   int32_t sink, window, sw_window, ring_slots;  // ring_slots = sink + window
   int32_t block_size, block_shift, max_batch, max_blocks;
   int32_t focus;
@@ -29,7 +29,8 @@ struct Plan {
   int16_t kidx[ODA_MAX_LAYERS];  // rank of the layer among layers of its kind
   int32_t full_splits, local_splits, sw_splits;
   int32_t tile_rows;  // rows one workgroup consumes per iteration
-  float scale_log2;   // softmax scale * log2(e)
+  float scale_log2;   // softmax scale * k_scale * log2(e)
+  float v_scale;
   int64_t recall_flops;
 };
 
@@ -83,7 +84,8 @@ struct AttnParams {
   float* part_ml;             // [batch][Hq][splits][2]
   int32_t* tickets;           // [batch][Hkv], zero between launches
   uint32_t* err;
-  float scale_log2;
+  float scale_log2;           // softmax scale * k_scale * log2(e)
+  float v_scale;              // applied to the merged output
 };
 
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.

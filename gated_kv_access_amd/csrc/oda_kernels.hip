@@ -7,10 +7,10 @@
 // device-side conditional Full pass).
 //
 // Attention is split-K flash decoding, one kernel per layer pass.  A workgroup
-// of four wave64s owns one (split, KV head, request) and streams its rows of K
-// and V with 16-byte loads: every lane holds four 16-byte chunks of a row, so a
-// 256-byte row (bf16, d = 128) is spread over 4 lanes and one wave covers 16
-// rows per pass.  All query heads of a GQA group use each loaded row.  Scores
+// of eight wave64s owns one (split, KV head, request) and streams its rows of
+// K and V with 16-byte loads: every lane holds four 16-byte chunks of a row, so
+// a 256-byte row (bf16, d = 128) is spread over 4 lanes and one wave covers 16
+// rows per pass (FP8 E4M3 rows: two chunks per lane, two passes per tile).  All query heads of a GQA group use each loaded row.  Scores
 // are reduced across the lanes of a row with DPP, the running maximum is kept
 // per wave (log2 domain, fp32), and each workgroup leaves one (o, m, l) partial
 // per query head.  The last workgroup of each (request, KV head) to finish --
@@ -119,18 +119,61 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// FP8 E4M3 (OCP encoding) to bf16 pairs and f32 pairs.  The gfx950
+// conversion instructions decode this encoding exactly, and every E4M3 value
+// is exact in bf16, so K can feed the bf16 dot instruction unchanged.  HI
+// selects bytes 2..3 of the word instead of bytes 0..1.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  lo = f[0];
+  hi = f[1];
+}
+
+// Register geometry of one K/V row.  A row is spread over LPR lanes; each lane
+// holds NV 16-byte vectors of it (bf16 / f32: four, FP8: two, so an FP8 lane
+// keeps the same 32 elements per row as a bf16 lane and the freed tile
+// registers carry a second pass of rows instead).
 template <int DT, int D>
 struct Geo {
-  static constexpr int ES = DT == ODA_BF16 ? 2 : 4;
+  static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
+  static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
+  static constexpr int NV = DT == ODA_FP8_E4M3 ? 2 : 4;  // 16-byte K/V vectors per lane per row
   static constexpr int ROW_BYTES = D * ES;
-  static constexpr int LPR = ROW_BYTES / 64;  // lanes sharing a row
-  static constexpr int RPP = kWave / LPR;     // rows per wave pass
-  static constexpr int EPV = 16 / ES;         // elements per 16-byte vector
-  static constexpr int EPL = 4 * EPV;         // elements per lane per row
-  static constexpr int NP = 1;                // passes per wave per tile
+  static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
+  static constexpr int RPP = kWave / LPR;            // rows per wave pass
+  static constexpr int EPV = 16 / ES;                // elements per 16-byte K/V vector
+  static constexpr int EPL = NV * EPV;               // elements per lane per row
+  static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
+  static constexpr int QPV = QV / NV;                // query vectors per K/V vector
+  static constexpr int NP = DT == ODA_FP8_E4M3 ? 2 : 1;  // passes per wave per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 8, "row must span 2..8 lanes");
+  static_assert(QV % NV == 0, "whole query vectors per K/V vector");
 };
+
+// One element of a stored K/V row and of a query row, widened to f32.
+template <int DT>
+__device__ __forceinline__ float kv_elem(const char* row, int e) {
+  if constexpr (DT == ODA_F32) {
+    return reinterpret_cast<const float*>(row)[e];
+  } else if constexpr (DT == ODA_BF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
+  } else {
+    float lo, hi;
+    fp8x2_to_f32<false>((uint32_t) reinterpret_cast<const uint8_t*>(row)[e], lo, hi);
+    return lo;
+  }
+}
+template <int DT>
+__device__ __forceinline__ float q_elem(const char* row, int e) {
+  if constexpr (DT == ODA_F32) return reinterpret_cast<const float*>(row)[e];
+  else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
+}
 
 // ----------------------------------------------------------------------------
 // access-set index code (shared by every kernel that turns rows into positions)
@@ -316,7 +359,7 @@ constexpr int kMergeBatch = 32;  // partials loaded per round by one output thre
 // outputs all belong to one head).  No LDS, no barrier.
 template <int DT, int D, int G>
 __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t used) {
-  constexpr int ES = DT == ODA_BF16 ? 2 : 4;
+  constexpr int ES = Geo<DT, D>::ES, QES = Geo<DT, D>::QES;
   constexpr int EPT = D / kWave;
   constexpr int GD = G * D;
   static_assert(GD <= kGroupThreads && GD % kWave == 0, "one thread per output, whole waves per head");
@@ -327,26 +370,16 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
 
   // current token: score (wave-wide dot product) and value element
-  const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * ES;
+  const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * QES;
   const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
   const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
   float dot = 0.f;  // every wave of head h computes the same q.k_cur, EPT elements per lane
 #pragma unroll
   for (int c = 0; c < EPT; ++c) {
     const int ee = lane * EPT + c;
-    float qx, kx;
-    if constexpr (DT == ODA_BF16) {
-      qx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[ee] << 16);
-      kx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(krow)[ee] << 16);
-    } else {
-      qx = reinterpret_cast<const float*>(qrow)[ee];
-      kx = reinterpret_cast<const float*>(krow)[ee];
-    }
-    dot = fmaf(qx, kx, dot);
+    dot = fmaf(q_elem<DT>(qrow, ee), kv_elem<DT>(krow, ee), dot);
   }
-  float vx;
-  if constexpr (DT == ODA_BF16) vx = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[e] << 16);
-  else vx = reinterpret_cast<const float*>(vrow)[e];
+  const float vx = kv_elem<DT>(vrow, e);
 
   const float* ml = P.part_ml + (head0 + h) * P.splits * 2;
   const float* po = P.part_o + (head0 + h) * P.splits * D + e;
@@ -382,7 +415,7 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
     L = fmaf(w, collect(ml + 2 * i + 1), L);
     acc = fmaf(w, collect(po + (int64_t)i * D), acc);
   }
-  P.out[(head0 + h) * D + e] = acc / L;
+  P.out[(head0 + h) * D + e] = acc / L * P.v_scale;
   if (P.lse != nullptr && e == 0) P.lse[head0 + h] = (M + __log2f(L)) * kLn2;
 }
 
@@ -393,8 +426,9 @@ template <int DT, int D, int G, int SRC, bool BALLOT>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
   using Gm = Geo<DT, D>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
+  constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
   constexpr int TILE = Gm::TILE;
-  constexpr int ES = Gm::ES;
+  constexpr int ES = Gm::ES, QES = Gm::QES;
 
   // The request this workgroup serves and its committed length (-1 = none).
   int32_t b;
@@ -455,14 +489,16 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   const int rrow = lane / LPR;
 
   // Query heads g*G .. g*G+G-1, in this lane's element slots.
-  uint4 qv[G][4];
+  // Query vector j covers the elements of K/V vector j / QPV.
+  uint4 qv[G][QV];
   {
-    const char* qbase = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + (int64_t)g * G) * D * ES;
+    const char* qbase = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + (int64_t)g * G) * D * QES;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qv[h][j] = *reinterpret_cast<const uint4*>(qbase + (int64_t)h * D * ES + (j * LPR + sub) * 16);
+      for (int j = 0; j < QV; ++j)
+        qv[h][j] = *reinterpret_cast<const uint4*>(qbase + (int64_t)h * D * QES +
+                                                   ((j / QPV) * LPR + sub) * EPV * QES + (j % QPV) * 16);
   }
 
   const char* kbase = static_cast<const char*>(P.k_base);
@@ -485,8 +521,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   // Tile registers: K and V of NP passes plus their validity.  Two sets
   // ping-pong so the loads of tile i+1 are in flight while tile i is reduced.
   struct TileRegs {
-    uint4 k[NP][4];
-    uint4 v[NP][4];
+    uint4 k[NP][NV];
+    uint4 v[NP][NV];
     bool valid[NP];  // paged: row in the pass; ring: row inside the ring (membership checked later)
     int32_t row[NP];
   };
@@ -532,7 +568,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       }
       R.valid[i] = ok;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NV; ++j) {
         if (ok) {
           R.k[i][j] = *reinterpret_cast<const uint4*>(kbase + off + (j * LPR + sub) * 16);
           R.v[i][j] = *reinterpret_cast<const uint4*>(vbase + off + (j * LPR + sub) * 16);
@@ -554,7 +590,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
         if (R.valid[i]) ring_slot_position(rst, R.row[i], in_local);
         R.valid[i] = in_local;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NV; ++j)
           if (!in_local) R.v[i][j] = make_uint4(0, 0, 0, 0);
       }
     }
@@ -562,14 +598,37 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     float s[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+      // FP8 keys become bf16 pairs once per row, shared by the G heads.
+      uint32_t kb[DT == ODA_FP8_E4M3 ? 2 * 4 * NV : 1];
+      if constexpr (DT == ODA_FP8_E4M3) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t w4[4] = {R.k[i][j].x, R.k[i][j].y, R.k[i][j].z, R.k[i][j].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kb[8 * j + 2 * c] = fp8x2_to_bf16x2<false>(w4[c]);
+            kb[8 * j + 2 * c + 1] = fp8x2_to_bf16x2<true>(w4[c]);
+          }
+        }
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NV; ++j) {
           const uint4 kk = R.k[i][j];
-          const uint4 qq = qv[h][j];
-          if constexpr (DT == ODA_BF16) {
+          const uint4 qq = qv[h][j * QPV];
+          if constexpr (DT == ODA_FP8_E4M3) {
+            const uint4 q1 = qv[h][j * QPV + 1];
+            acc = dot2_bf16(kb[8 * j + 0], qq.x, acc);
+            acc = dot2_bf16(kb[8 * j + 1], qq.y, acc);
+            acc = dot2_bf16(kb[8 * j + 2], qq.z, acc);
+            acc = dot2_bf16(kb[8 * j + 3], qq.w, acc);
+            acc = dot2_bf16(kb[8 * j + 4], q1.x, acc);
+            acc = dot2_bf16(kb[8 * j + 5], q1.y, acc);
+            acc = dot2_bf16(kb[8 * j + 6], q1.z, acc);
+            acc = dot2_bf16(kb[8 * j + 7], q1.w, acc);
+          } else if constexpr (DT == ODA_BF16) {
             acc = dot2_bf16(kk.x, qq.x, acc);
             acc = dot2_bf16(kk.y, qq.y, acc);
             acc = dot2_bf16(kk.z, qq.z, acc);
@@ -612,11 +671,22 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
         l_acc[h] += pr[h];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NV; ++j) {
         const uint32_t w4[4] = {R.v[i][j].x, R.v[i][j].y, R.v[i][j].z, R.v[i][j].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if constexpr (DT == ODA_BF16) {
+          if constexpr (DT == ODA_FP8_E4M3) {
+            float v0, v1, v2, v3;
+            fp8x2_to_f32<false>(w4[c], v0, v1);
+            fp8x2_to_f32<true>(w4[c], v2, v3);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              o[h][j * EPV + 4 * c] = fmaf(pr[h], v0, o[h][j * EPV + 4 * c]);
+              o[h][j * EPV + 4 * c + 1] = fmaf(pr[h], v1, o[h][j * EPV + 4 * c + 1]);
+              o[h][j * EPV + 4 * c + 2] = fmaf(pr[h], v2, o[h][j * EPV + 4 * c + 2]);
+              o[h][j * EPV + 4 * c + 3] = fmaf(pr[h], v3, o[h][j * EPV + 4 * c + 3]);
+            }
+          } else if constexpr (DT == ODA_BF16) {
             const float v0 = bf16_lo(w4[c]);
             const float v1 = bf16_hi(w4[c]);
 #pragma unroll
@@ -682,7 +752,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int c = 0; c < EPV; c += 4)
           *reinterpret_cast<float4*>(&s_o[wr][h][(j * LPR + sub) * EPV + c]) =
@@ -1152,6 +1222,7 @@ int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_st
 
 int tile_rows_for(int32_t dtype, int32_t head_dim) {
   if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128>::TILE : Geo<ODA_BF16, 64>::TILE;
+  if (dtype == ODA_FP8_E4M3) return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128>::TILE : Geo<ODA_FP8_E4M3, 64>::TILE;
   return head_dim == 128 ? Geo<ODA_F32, 128>::TILE : Geo<ODA_F32, 64>::TILE;
 }
 
@@ -1160,6 +1231,10 @@ int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stre
   if (p.dtype == ODA_BF16) {
     if (p.D == 128) return launch_attention_d<ODA_BF16, 128>(p, a, batch, s);
     return launch_attention_d<ODA_BF16, 64>(p, a, batch, s);
+  }
+  if (p.dtype == ODA_FP8_E4M3) {
+    if (p.D == 128) return launch_attention_d<ODA_FP8_E4M3, 128>(p, a, batch, s);
+    return launch_attention_d<ODA_FP8_E4M3, 64>(p, a, batch, s);
   }
   if (p.D == 128) return launch_attention_d<ODA_F32, 128>(p, a, batch, s);
   return launch_attention_d<ODA_F32, 64>(p, a, batch, s);

@@ -17,6 +17,11 @@ from . import binding as B
 from .workloads import Workload, gen_block_table, gen_focus, gen_sequence
 
 
+def _raw(x: torch.Tensor) -> torch.Tensor:
+    """E4M3 tensors are moved as their bytes."""
+    return x.view(torch.uint8) if x.dtype == torch.float8_e4m3fn else x
+
+
 def make_dims(wl: Workload, full_splits: int = 0, local_splits: int = 0,
               focus: Optional[bool] = None, recall_flops: int = 0) -> B.OdaDims:
     d = B.OdaDims()
@@ -30,11 +35,13 @@ def make_dims(wl: Workload, full_splits: int = 0, local_splits: int = 0,
     d.block_size = wl.block_size
     d.max_batch = wl.batch
     d.max_blocks_per_seq = wl.max_blocks_per_seq
-    d.kv_dtype = B.BF16 if wl.dtype == "bf16" else B.F32
+    d.kv_dtype = {"bf16": B.BF16, "f32": B.F32, "fp8": B.FP8_E4M3}[wl.dtype]
     d.focus = int(wl.focus if focus is None else focus)
     d.full_splits = full_splits
     d.local_splits = local_splits
     d.softmax_scale = 0.0
+    d.k_scale = wl.k_scale
+    d.v_scale = wl.v_scale
     d.reserved0 = 0
     d.recall_flops = recall_flops
     kinds = np.ascontiguousarray(np.array(wl.kinds, dtype=np.uint8))
@@ -102,7 +109,7 @@ class DecodeState:
         per-request arrays offset; caches unchanged since block ids are global)."""
         wl, kv = self.wl, B.OdaKV()
         ctypes.memmove(ctypes.byref(kv), ctypes.byref(self.kv), ctypes.sizeof(B.OdaKV))
-        es = 2 if wl.dtype == "bf16" else 4
+        es = wl.esize
         R, W = wl.sink + wl.window, wl.sw_window
         if self.k_ring is not None:
             step = wl.num_kv_heads * R * wl.head_dim * es
@@ -126,8 +133,8 @@ class DecodeState:
             P = wl.prefill[b]
             kv_b = self.shifted_kv(b)
             for layer in range(wl.num_layers):
-                k_src = self.sequence(layer, b, "k")[:max(P, 1)].unsqueeze(0).contiguous()
-                v_src = self.sequence(layer, b, "v")[:max(P, 1)].unsqueeze(0).contiguous()
+                k_src = _raw(self.sequence(layer, b, "k"))[:max(P, 1)].unsqueeze(0).contiguous()
+                v_src = _raw(self.sequence(layer, b, "v"))[:max(P, 1)].unsqueeze(0).contiguous()
                 B.prefill_kv(self.dims, kv_b, 1, layer, k_src, v_src, k_src.shape[1], self.workspace)
                 del k_src, v_src
         torch.cuda.synchronize(self.device)
@@ -143,8 +150,8 @@ class DecodeState:
         for layer in range(wl.num_layers):
             for b in range(wl.batch):
                 P = wl.prefill[b]
-                k_new[:, layer, b] = self.sequence(layer, b, "k")[P:P + n]
-                v_new[:, layer, b] = self.sequence(layer, b, "v")[P:P + n]
+                _raw(k_new)[:, layer, b] = _raw(self.sequence(layer, b, "k"))[P:P + n]
+                _raw(v_new)[:, layer, b] = _raw(self.sequence(layer, b, "v"))[P:P + n]
         return k_new, v_new
 
     def device_error(self) -> int:

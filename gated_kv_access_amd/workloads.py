@@ -10,7 +10,10 @@ The shapes follow the runtime setting of the On-Demand Attention pages
 with a Qwen3-1.7B-like attention shape (28 layers, 16 query / 8 KV heads of
 128, bf16).  No dataset or trained weight is involved: keys, values and
 queries are N(0,1) draws rounded to the storage type, and recall scores are
-drawn so that the Full-call rate is the stated rho.
+drawn so that the Full-call rate is the stated rho.  FP8 E4M3 variants of a
+workload (``Workload.fp8()``) store K/V as E4M3 codes of N(0, 16^2) draws with
+per-tensor scales 1/16, so that the dequantised values are again about N(0,1);
+their queries stay bf16.
 """
 from __future__ import annotations
 
@@ -30,7 +33,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str                      # "bf16" or "f32"
+    dtype: str                      # K/V storage: "bf16", "f32" or "fp8" (E4M3; queries then bf16)
     batch: int
     prefill: Tuple[int, ...]        # committed positions per request before step 1
     steps: int
@@ -44,14 +47,28 @@ class Workload:
     rho: Tuple[float, ...] = (0.5,)  # per request (one value = all requests)
     seed: int = 0
     block_order: str = "shuffled"   # physical block ids: "shuffled" (seeded permutation) or "sequential"
+    k_scale: float = 1.0            # K = k_scale * stored value
+    v_scale: float = 1.0
+    kv_code_std: float = 1.0        # standard deviation of the stored K/V draws
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        """Storage type of K and V."""
+        return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[self.dtype]
+
+    @property
+    def q_torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
     @property
     def esize(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        """Bytes per stored K/V element."""
+        return {"bf16": 2, "f32": 4, "fp8": 1}[self.dtype]
+
+    def fp8(self, k_scale: float = 0.0625, v_scale: float = 0.0625, code_std: float = 16.0) -> "Workload":
+        """The same workload with an FP8 E4M3 KV cache."""
+        return replace(self, name=self.name + "_fp8e4m3", dtype="fp8", k_scale=k_scale, v_scale=v_scale,
+                       kv_code_std=code_std)
 
     @property
     def kinds(self) -> Tuple[int, ...]:
@@ -131,11 +148,13 @@ def _seed(*parts: int) -> int:
     return int(np.random.SeedSequence([int(p) for p in parts]).generate_state(1)[0])
 
 
-def _normal(shape, seed: int, device, dtype: torch.dtype) -> torch.Tensor:
+def _normal(shape, seed: int, device, dtype: torch.dtype, std: float = 1.0) -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    return x.to(dtype)  # round-to-nearest-even for bf16
+    if std != 1.0:
+        x = x * std
+    return x.to(dtype)  # round-to-nearest-even (bf16, E4M3)
 
 
 def gen_sequence(wl: Workload, layer: int, b: int, which: str, device="cpu") -> torch.Tensor:
@@ -143,14 +162,14 @@ def gen_sequence(wl: Workload, layer: int, b: int, which: str, device="cpu") -> 
     Row p-1 holds position p; rows >= prefill[b] are the tokens decoded at steps 1.."""
     tag = {"k": 1, "v": 2}[which]
     return _normal((wl.rows(b), wl.num_kv_heads, wl.head_dim),
-                   _seed(wl.seed, 11, layer, b, tag), device, wl.torch_dtype)
+                   _seed(wl.seed, 11, layer, b, tag), device, wl.torch_dtype, wl.kv_code_std)
 
 
 def gen_queries(wl: Workload, device="cpu", steps: Optional[int] = None, tag: int = 3) -> torch.Tensor:
     """Per-step queries [steps][L][B][Hq][d]."""
     n = wl.steps if steps is None else steps
     return _normal((n, wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim),
-                   _seed(wl.seed, 13, tag), device, wl.torch_dtype)
+                   _seed(wl.seed, 13, tag), device, wl.q_torch_dtype)
 
 
 def gen_scores(wl: Workload, steps: Optional[int] = None, rho: Optional[Tuple[float, ...]] = None) -> np.ndarray:

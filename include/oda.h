@@ -17,8 +17,11 @@
  *     buffer and the stream; the library keeps no state between calls, never
  *     allocates, never synchronises, and launches only kernels (no memset or
  *     memcpy nodes), so every call may be recorded into a HIP graph.
- *   - Element type of q, K and V is oda_dims.kv_dtype (bf16 or f32); outputs
- *     and lse are always f32; accumulation is f32.
+ *   - Element type of K and V (caches, rings, k_cur/v_cur, k_new/v_new, prefill
+ *     sources) is oda_dims.kv_dtype.  Queries are of the same type for bf16
+ *     and f32, and bf16 when K/V are FP8 E4M3.  Stored K and V values are
+ *     multiplied by oda_dims.k_scale / v_scale (per-tensor dequantisation
+ *     scales, any dtype).  Outputs and lse are always f32; accumulation is f32.
  *   - seq_len[b] is the number of committed positions of request b.  During a
  *     step the token being decoded is at position t = seq_len[b] + 1 and its
  *     K/V come from the k_cur/v_cur (or k_new/v_new) arguments, not from the
@@ -51,7 +54,13 @@ typedef enum {
   ODA_ERR_WORKSPACE = -4     /* workspace missing or smaller than required    */
 } oda_status;
 
-typedef enum { ODA_BF16 = 0, ODA_F32 = 1 } oda_dtype;
+/* ODA_FP8_E4M3: one byte per element in the OCP OFP8 E4M3 encoding (bias 7,
+ * no infinities, largest finite 448).  Quantising the stored KV is the
+ * complementary technique of the kongchang.com Declarative Attention page,
+ * section "The KV Cache Compression Technology Ecosystem"; the codes are
+ * produced by the caller (the projection that makes K/V), the library only
+ * stores, moves and dequantises them. */
+typedef enum { ODA_BF16 = 0, ODA_F32 = 1, ODA_FP8_E4M3 = 2 } oda_dtype;
 
 /* Layer kinds.  GATED layers have distinct Local (sinks + window, served from
  * the ring) and Full (whole paged cache) access sets.  SLIDING layers (hybrid
@@ -95,6 +104,8 @@ typedef struct {
                                   or focus pass; 0 = library default                     */
   int32_t local_splits;        /* same for ring passes; 0 = default                      */
   float   softmax_scale;       /* 0 -> 1/sqrt(head_dim)                                  */
+  float   k_scale;             /* K = k_scale * stored value; 0 -> 1                     */
+  float   v_scale;             /* V = v_scale * stored value; 0 -> 1                     */
   int32_t reserved0;           /* must be 0                                              */
   int64_t recall_flops;        /* F_Recall charged per request per step (accounting)     */
   const uint8_t* layer_kind;   /* host [num_layers] of oda_layer_kind; NULL = all GATED  */

@@ -16,30 +16,35 @@ from gated_kv_access_amd.state import DecodeState
 # Output bars.  bf16 inputs: max-abs 1e-2 and relative L2 2e-3 per (step, layer)
 # output tensor.  f32 inputs: see the tolerance derivation of the design notes
 # (fp32 accumulation over at most a few thousand positions).
-TOL = {"bf16": (1e-2, 2e-3), "f32": (1e-4, 1e-5)}
-LSE_TOL = {"bf16": 1e-3, "f32": 1e-4}
+# FP8 E4M3 K/V: both sides read the same codes, the queries are bf16 and the
+# kernel's arithmetic is that of the bf16 path, so the bf16 bars apply.
+TOL = {"bf16": (1e-2, 2e-3), "f32": (1e-4, 1e-5), "fp8": (1e-2, 2e-3)}
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-4, "fp8": 1e-3}
+ORACLE_DTYPE = {"bf16": orc.BF16, "f32": orc.F32, "fp8": orc.FP8}
 
 
 def words(x: torch.Tensor) -> np.ndarray:
     x = x.detach().cpu().contiguous()
     if x.dtype == torch.bfloat16:
         return x.view(torch.int16).numpy().view(np.uint16)
+    if x.dtype == torch.float8_e4m3fn:
+        return x.view(torch.uint8).numpy()
     return x.to(torch.float32).numpy()
 
 
 def oracle_cfg(wl: W.Workload, focus=None, recall_flops: int = 0) -> orc.OracleConfig:
     return orc.OracleConfig(wl.num_layers, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, sink=wl.sink,
                             window=wl.window, sw_window=wl.sw_window,
-                            dtype=orc.BF16 if wl.dtype == "bf16" else orc.F32,
+                            dtype=ORACLE_DTYPE[wl.dtype],
                             focus=wl.focus if focus is None else focus, recall_flops=recall_flops,
-                            layer_kind=list(wl.kinds))
+                            layer_kind=list(wl.kinds), k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
 def oracle_sequences(st: DecodeState):
     """[L][B][T][Hkv][d] raw words of every request's rows, redrawn on the generator device."""
     wl = st.wl
     T = wl.max_rows
-    dt = np.uint16 if wl.dtype == "bf16" else np.float32
+    dt = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[wl.dtype]
     ks = np.zeros((wl.num_layers, wl.batch, T, wl.num_kv_heads, wl.head_dim), dtype=dt)
     vs = np.zeros_like(ks)
     for l in range(wl.num_layers):

@@ -39,7 +39,8 @@ def _dims(**kw):
     d = B.OdaDims()
     base = dict(num_layers=2, num_q_heads=4, num_kv_heads=2, head_dim=128, sink=4, window=64,
                 sw_window=0, block_size=16, max_batch=3, max_blocks_per_seq=40, kv_dtype=B.BF16,
-                focus=0, full_splits=0, local_splits=0, softmax_scale=0.0, reserved0=0, recall_flops=0)
+                focus=0, full_splits=0, local_splits=0, softmax_scale=0.0, k_scale=0.0, v_scale=0.0,
+                reserved0=0, recall_flops=0)
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
@@ -71,6 +72,18 @@ def test_workspace_size_valid_and_invalid(lib):
     assert lib.oda_workspace_size(ctypes.byref(_dims(reserved0=1)), 1) == 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(head_dim=96)), 1) == 0        # not built
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2)), 1) == 0  # group 8
+    assert lib.oda_workspace_size(ctypes.byref(_dims(kv_dtype=3)), 1) == 0
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert lib.oda_workspace_size(ctypes.byref(_dims(k_scale=bad)), 1) == 0
+        assert lib.oda_workspace_size(ctypes.byref(_dims(v_scale=bad)), 1) == 0
+
+
+def test_fp8_dims_accepted_and_workspace_independent_of_kv_dtype(lib):
+    """The split partials are f32 whatever the stored type, so the workspace
+    of an FP8 E4M3 cache differs from bf16 only through the split counts."""
+    for d in (128, 64):
+        n8 = lib.oda_workspace_size(ctypes.byref(_dims(kv_dtype=B.FP8_E4M3, head_dim=d, k_scale=0.05, v_scale=3.0)), 3)
+        assert n8 > 256 and n8 % 256 == 0
 
 
 def _ws(lib, d, batch=3):

@@ -83,7 +83,8 @@ def _check(wl, st, q, scores, r, rec, sample_layers, sample_requests):
                     mode = orc.FULL if fired[k, b] else orc.LOCAL
                     pos = orc.access_set(cfg, kind, mode, t, int(focus[b, 0]), int(focus[b, 1]))
                     for h in range(wl.num_q_heads):
-                        jobs[(k, h)] = ex.submit(orc.attention, qh[k, l, b, h], ks, vs, h // G, pos, cfg.dtype)
+                        jobs[(k, h)] = ex.submit(orc.attention, qh[k, l, b, h], ks, vs, h // G, pos, cfg.dtype,
+                                                 0.0, cfg.k_scale, cfg.v_scale)
                 for k in rec:
                     want = np.stack([jobs[(k, h)].result()[0] for h in range(wl.num_q_heads)])
                     got = rec[k][0][li, bi].astype(np.float64)
@@ -132,3 +133,18 @@ def test_hybrid_sliding_and_focus_sampled(focus):
     steps = 10
     out = _run_and_sample(wl, steps, {0, steps - 1}, (2, 3, 31), (0, 5))
     _check(*out, (2, 3, 31), (0, 5))
+
+
+def test_ctx128k_rho0125_fp8_kv_sampled():
+    """The 128K workload with an E4M3 KV cache (per-tensor scales 1/16)."""
+    wl = W.config(2).fp8()
+    steps = 48
+    out = _run_and_sample(wl, steps, {0, 7, steps - 1}, (0, 27), (0,))
+    _check(*out, (0, 27), (0,))
+
+
+def test_hybrid_focus_fp8_kv_sampled():
+    wl = W.config(4).fp8()
+    steps = 8
+    out = _run_and_sample(wl, steps, {0, steps - 1}, (3, 31), (0, 7))
+    _check(*out, (3, 31), (0, 7))

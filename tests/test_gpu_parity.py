@@ -270,3 +270,55 @@ def test_standalone_local_and_gated_full_calls():
         assert torch.equal(out[1], local[1]), "a request that did not fire keeps its Local row"
         assert_outputs_close(out.cpu().numpy()[None, None], want["out"][:, layer:layer + 1], wl.dtype,
                              f"standalone layer {layer}")
+
+
+# ---------------------------------------------------------------- FP8 E4M3 KV cache
+
+FP8 = [
+    _small("d128_g2", seed=131).fp8(),
+    _small("d64_g1", head_dim=64, num_q_heads=2, num_kv_heads=2, seed=132).fp8(),
+    _small("d128_g4", num_q_heads=8, num_kv_heads=2, seed=133).fp8(),
+    _small("d64_g4_bs8_odd_scales", head_dim=64, num_q_heads=4, num_kv_heads=1, block_size=8,
+           seed=134).fp8(k_scale=0.0371, v_scale=2.5, code_std=8.0),
+    _small("ring_wrap_bs64", sink=2, window=16, prefill=(100, 37, 5), steps=40, block_size=64, seed=135).fp8(),
+    _small("hybrid_focus", num_layers=8, sw_window=64, sink=4, window=128, batch=3,
+           prefill=(1000, 2500, 6000), steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)),
+           focus=True, seed=136).fp8(),
+]
+
+
+@pytest.mark.parametrize("wl", FP8, ids=[w.name for w in FP8])
+def test_fp8_kv_runs_match_oracle(wl):
+    """E4M3 codes in the caches, rings and new-token inputs, bf16 queries,
+    per-tensor dequantisation scales; outputs to the bf16 bars."""
+    _check_run(wl)
+
+
+def test_fp8_graph_replay_matches_eager():
+    wl = _small("graph", prefill=(50, 900, 2100), steps=12, seed=137).fp8()
+    _, g_run, _ = _check_run(wl, graph=True)
+    _, e_run, _ = _check_run(wl, graph=False)
+    assert np.array_equal(g_run.out, e_run.out)
+
+
+def test_fp8_equals_bf16_path_on_the_same_values():
+    """Every E4M3 value is exact in bf16: the FP8 path with unit scales and
+    the bf16 path over the decoded values see the same numbers, so their
+    outputs agree to fp32 summation-order rounding."""
+    wl8 = _small("same_values", prefill=(0, 700, 3001), steps=6, seed=138).fp8(k_scale=1.0, v_scale=1.0,
+                                                                              code_std=1.0)
+    st8 = DecodeState(wl8, gen_device="cpu")
+    st8.prefill()
+    q = W.gen_queries(wl8, "cpu")
+    scores = W.gen_scores(wl8)
+    r8 = run_steps(st8, q, scores)
+    # the bf16 state holds the decoded values of the same codes
+    wlb = wl8.with_(dtype="bf16", name="same_values_bf16")
+    stb = DecodeState(wlb, gen_device="cpu")
+    stb.sequence = lambda layer, b, which: W.gen_sequence(wl8, layer, b, which, "cpu").to(torch.bfloat16).to(stb.device)
+    stb.prefill()
+    rb = run_steps(stb, q, scores)
+    assert np.array_equal(r8.counters[:, :6], rb.counters[:, :6])
+    diff = float(np.abs(r8.out - rb.out).max())
+    say(f"fp8 vs bf16 path on identical values: max diff {diff:.3e}")
+    assert diff <= 2e-5
