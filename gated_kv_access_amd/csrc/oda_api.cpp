@@ -92,7 +92,7 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
   const int32_t b = batch > 0 ? batch : 1;
   if (p->Lg > 0) {
     const int64_t max_ctx = (int64_t)p->max_blocks * p->block_size;
-    const int32_t tiles = ceil_div(max_ctx, tile);
+    const int32_t tiles = ceil_div(max_ctx + 1, tile);  // + 1: the current token is a row too
     int32_t f = d->full_splits;
     if (f <= 0) {
       // Whole rounds of kComputeUnits workgroups: `round` splits per (request,
@@ -106,14 +106,14 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     if (f > tiles) f = tiles;
     if (f > kMaxSplits) f = kMaxSplits;
     p->full_splits = f < 1 ? 1 : f;
-    const int32_t rtiles = ceil_div(p->ring_slots, tile);
+    const int32_t rtiles = ceil_div(p->ring_slots + 1, tile);
     int32_t l = d->local_splits > 0 ? d->local_splits : rtiles;  // one tile per workgroup
     if (l > rtiles) l = rtiles;
     if (l > kMaxSplits) l = kMaxSplits;
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
-    const int32_t stiles = ceil_div(p->sw_window, tile);
+    const int32_t stiles = ceil_div(p->sw_window + 1, tile);
     int32_t s = d->local_splits > 0 ? d->local_splits : stiles;
     if (s > stiles) s = stiles;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -191,7 +191,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
                     const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
                     const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
                     const float* score, float theta, int32_t* list_out, int32_t* count_out,
-                    oda_stream s) {
+                    oda_stream s, int32_t warm_layer = -1) {
   const Plan& p = c.plan;
   const bool gated = p.kind[layer] == ODA_LAYER_GATED;
   const bool full = gate != oda::kGateAll;
@@ -242,6 +242,14 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
+  if (warm_layer >= 0 && a.rows.source == oda::kSrcRing) {
+    const bool wg = p.kind[warm_layer] == ODA_LAYER_GATED;
+    const int32_t slots = wg ? p.ring_slots : p.sw_window;
+    const int64_t layer_bytes = (int64_t)p.max_batch * p.Hkv * slots * row_bytes;
+    a.pf_k = static_cast<const char*>(wg ? kv->k_ring : kv->k_swring) + p.kidx[warm_layer] * layer_bytes;
+    a.pf_v = static_cast<const char*>(wg ? kv->v_ring : kv->v_swring) + p.kidx[warm_layer] * layer_bytes;
+    a.pf_slots = slots;
+  }
   return hip_status(oda::launch_attention(p, a, batch, s));
 }
 
@@ -368,7 +376,7 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   for (int32_t l = 0; l < p.L; ++l) {
     st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream, l + 1 < p.L ? l + 1 : -1);
     if (st != ODA_OK) return st;
   }
   // 2) Gate: compaction of the fired requests, counters.

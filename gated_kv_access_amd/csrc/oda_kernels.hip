@@ -33,10 +33,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 template <int MASK>
 __device__ __forceinline__ float xor_lane(float v) {
   const int x = __float_as_int(v);
+  // DPP forms read a valid lane everywhere, so bound_ctrl changes nothing but
+  // lets the compiler fold the move into the consuming add.
   if constexpr (MASK == 1) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
   } else if constexpr (MASK == 2) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
   } else if constexpr (MASK < 32) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10)));      // xor within 32
   } else {
@@ -70,7 +72,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // modifier: no LDS traffic and no wait).
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, true));
 }
 
 // Sum / max over the lanes of a 16-lane row that are congruent modulo STEP
@@ -350,70 +352,48 @@ __device__ void write_call_list(const AttnParams& P) {
 // ----------------------------------------------------------------------------
 // merge of the split partials and the current token (run by one workgroup)
 
-constexpr int kMaxMergeSplits = 512;
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
-// One thread per output element (h, e): it loads every partial (m, l, o[e])
-// of its head in rounds of kMergeBatch -- one round when used <= 32 -- and the
-// current token's score comes from a dot product across its wave (a wave's
-// outputs all belong to one head).  No LDS, no barrier.
+// One thread per output element (h, e); a wave serves one head.  Partials
+// are taken in rounds of up to kMergeBatch: lane i loads (m, l) of partial i
+// of the round (one 8-byte load), every lane loads its element of each
+// partial's o, the round's maximum and weights come from lane exchanges, and
+// the weights reach every lane by lane reads.  The current token is a row of
+// the last split, so only partials are combined here.  No LDS, no barrier.
 template <int DT, int D, int G>
 __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t used) {
-  constexpr int ES = Geo<DT, D>::ES, QES = Geo<DT, D>::QES;
-  constexpr int EPT = D / kWave;
   constexpr int GD = G * D;
-  static_assert(GD <= kGroupThreads && GD % kWave == 0, "one thread per output, whole waves per head");
+  static_assert(GD <= kGroupThreads && D % kWave == 0, "one thread per output, one head per wave");
   const int tid = threadIdx.x;
   if (tid >= GD) return;
   const int lane = tid & (kWave - 1);
   const int h = tid / D, e = tid % D;
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
-
-  // current token: score (wave-wide dot product) and value element
-  const char* qrow = static_cast<const char*>(P.q) + (head0 + h) * D * QES;
-  const char* krow = static_cast<const char*>(P.k_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-  const char* vrow = static_cast<const char*>(P.v_cur) + ((int64_t)b * P.Hkv + g) * D * ES;
-  float dot = 0.f;  // every wave of head h computes the same q.k_cur, EPT elements per lane
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) {
-    const int ee = lane * EPT + c;
-    dot = fmaf(q_elem<DT>(qrow, ee), kv_elem<DT>(krow, ee), dot);
-  }
-  const float vx = kv_elem<DT>(vrow, e);
-
   const float* ml = P.part_ml + (head0 + h) * P.splits * 2;
   const float* po = P.part_o + (head0 + h) * P.splits * D + e;
-  float m[kMergeBatch], l[kMergeBatch], x[kMergeBatch];
-  const int n0 = used < kMergeBatch ? used : kMergeBatch;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int32_t base = 0; base < used; base += kMergeBatch) {
+    const int32_t n = used - base < kMergeBatch ? used - base : kMergeBatch;
+    float x[kMergeBatch];
 #pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i) {
-    if (i < n0) {
-      m[i] = collect(ml + 2 * i);
-      l[i] = collect(ml + 2 * i + 1);
-      x[i] = collect(po + (int64_t)i * D);
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i < n) x[i] = collect(po + (int64_t)(base + i) * D);
+    float mi = -INFINITY, li = 0.f;
+    if (lane < n) {
+      const uint64_t w2 = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(ml + 2 * (base + lane))),
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mi = __uint_as_float((uint32_t)w2);
+      li = __uint_as_float((uint32_t)(w2 >> 32));
     }
-  }
-  const float s_cur = sum_over<1, 32>(dot) * P.scale_log2;
-  float M = s_cur;
+    const float m_new = fmaxf(M, max_over<1, 32>(mi));
+    const float keep = M == -INFINITY ? 0.f : fast_exp2(M - m_new);
+    const float wi = mi == -INFINITY ? 0.f : fast_exp2(mi - m_new);
+    L = fmaf(L, keep, sum_over<1, 32>(wi * li));
+    acc *= keep;
 #pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i)
-    if (i < n0) M = fmaxf(M, m[i]);
-  for (int i = kMergeBatch; i < used; ++i) M = fmaxf(M, collect(ml + 2 * i));
-  const float wc = fast_exp2(s_cur - M);
-  float L = wc, acc = wc * vx;
-#pragma unroll
-  for (int i = 0; i < kMergeBatch; ++i) {
-    if (i < n0) {
-      const float w = m[i] == -INFINITY ? 0.f : fast_exp2(m[i] - M);
-      L = fmaf(w, l[i], L);
-      acc = fmaf(w, x[i], acc);
-    }
-  }
-  for (int i = kMergeBatch; i < used; ++i) {
-    const float mi = collect(ml + 2 * i);
-    const float w = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
-    L = fmaf(w, collect(ml + 2 * i + 1), L);
-    acc = fmaf(w, collect(po + (int64_t)i * D), acc);
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i < n) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], acc);
+    M = m_new;
   }
   P.out[(head0 + h) * D + e] = acc / L * P.v_scale;
   if (P.lse != nullptr && e == 0) P.lse[head0 + h] = (M + __log2f(L)) * kLn2;
@@ -473,15 +453,13 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     iv = paged_intervals(P.rows, t, fa, fb);
     n_rows = iv.total;
   }
+  // Row n_rows is the current token t, read from k_cur / v_cur: it is
+  // processed like any other row, by the last split.
   int32_t per, used;
-  split_tiles(n_rows, TILE, P.splits, per, used);
-  if (used == 0) {  // t = 1 on a paged pass: only the current token
-    if (split == 0) merge_and_write<DT, D, G>(P, b, g, 0);
-    return;
-  }
+  split_tiles(n_rows + 1, TILE, P.splits, per, used);
   if (split >= used) return;
   const int32_t tile_begin = split * per;
-  const int32_t tile_end = min(tile_begin + per, (n_rows + TILE - 1) / TILE);
+  const int32_t tile_end = min(tile_begin + per, (n_rows + TILE) / TILE);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -508,6 +486,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     ring_head_off = (((int64_t)b * P.Hkv + g) * P.rows.ring_slots) * D * ES;
   const int32_t* btab = P.block_table + (int64_t)b * P.max_blocks;
   const int32_t bmask = (1 << P.block_shift) - 1;
+  const int64_t cur_off = ((int64_t)b * P.Hkv + g) * D * ES;
 
   float m_run[G], l_acc[G], o[G][EPL];
 #pragma unroll
@@ -550,9 +529,15 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     for (int i = 0; i < NP; ++i) {
       const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
       R.row[i] = row;
-      bool ok = row < n_rows;
+      bool ok = row <= n_rows;
+      const char* kb = kbase;
+      const char* vb = vbase;
       int64_t off = 0;
-      if constexpr (SRC == kSrcRing) {
+      if (row == n_rows) {
+        kb = static_cast<const char*>(P.k_cur);
+        vb = static_cast<const char*>(P.v_cur);
+        off = cur_off;
+      } else if constexpr (SRC == kSrcRing) {
         off = ring_head_off + (int64_t)row * D * ES;
       } else {
         if (ok) {
@@ -570,8 +555,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         if (ok) {
-          R.k[i][j] = *reinterpret_cast<const uint4*>(kbase + off + (j * LPR + sub) * 16);
-          R.v[i][j] = *reinterpret_cast<const uint4*>(vbase + off + (j * LPR + sub) * 16);
+          R.k[i][j] = *reinterpret_cast<const uint4*>(kb + off + (j * LPR + sub) * 16);
+          R.v[i][j] = *reinterpret_cast<const uint4*>(vb + off + (j * LPR + sub) * 16);
         } else {
           R.k[i][j] = make_uint4(0, 0, 0, 0);
           R.v[i][j] = make_uint4(0, 0, 0, 0);
@@ -586,8 +571,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       // yet written may hold anything, so their values are replaced by zeros).
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        bool in_local = false;
-        if (R.valid[i]) ring_slot_position(rst, R.row[i], in_local);
+        bool in_local = R.valid[i] && R.row[i] == n_rows;  // the current token
+        if (R.valid[i] && !in_local) ring_slot_position(rst, R.row[i], in_local);
         R.valid[i] = in_local;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -725,28 +710,55 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (has_b) process_tile(rb);
   }
 
-  // Epilogue 1: inside each 16-lane row, fold the row groups onto a common
-  // maximum with DPP; every lane then holds its row's sums for its `sub`.
+  // Epilogue 1: the workgroup's maximum reference per head (DPP inside each
+  // 16-lane row, lane reads across the four rows, one LDS exchange between
+  // waves); every lane then rescales its sums onto it and the row groups of
+  // each 16-lane row are added with DPP.  The partials left for the LDS fold
+  // share one maximum, so the fold is a plain sum.
   constexpr int kRows16 = kWave / 16;
+  constexpr int NWR = kWavesPerGroup * kRows16;
+  __shared__ float s_wmax[kWavesPerGroup][G];
+  constexpr int RS = G * D + 4;  // LDS row stride: the four 16-lane rows of a wave store to distinct banks
+  __shared__ float s_o[NWR][RS];
+  __shared__ float s_l[kWavesPerGroup][G];
+  __shared__ int32_t s_last;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mrow = row_group_max<LPR>(m_run[h]);
-    const float sc = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - mrow);
-    m_run[h] = mrow;
-    l_acc[h] = row_group_sum<LPR>(l_acc[h] * sc);
+    const int mr = __float_as_int(row_group_max<LPR>(m_run[h]));
+    const float m4 = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mr, 0)),
+                                 __int_as_float(__builtin_amdgcn_readlane(mr, 16))),
+                           fmaxf(__int_as_float(__builtin_amdgcn_readlane(mr, 32)),
+                                 __int_as_float(__builtin_amdgcn_readlane(mr, 48))));
+    if (lane == 0) s_wmax[wave][h] = m4;
+  }
+  __syncthreads();
+  float M[G];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = row_group_sum<LPR>(o[h][e] * sc);
+  for (int h = 0; h < G; ++h) {
+    M[h] = s_wmax[0][h];
+#pragma unroll
+    for (int w = 1; w < kWavesPerGroup; ++w) M[h] = fmaxf(M[h], s_wmax[w][h]);
+    const float sc = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - M[h]);
+    {
+#pragma clang fp contract(off)  // keep the scaling separate so each DPP move folds into an add
+      l_acc[h] = row_group_sum<LPR>(l_acc[h] * sc);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        o[h][e] = row_group_sum<LPR>(o[h][e] * sc);
+        asm volatile("" : "+v"(o[h][e]));  // the sums are complete here, not inside the store branch
+      }
+    }
+    // the wave's l: the four 16-lane rows' sums, read across lanes
+    const int li = __float_as_int(l_acc[h]);
+    const float lw = (__int_as_float(__builtin_amdgcn_readlane(li, 0)) + __int_as_float(__builtin_amdgcn_readlane(li, 16))) +
+                     (__int_as_float(__builtin_amdgcn_readlane(li, 32)) + __int_as_float(__builtin_amdgcn_readlane(li, 48)));
+    if (lane == 0) s_l[wave][h] = lw;
   }
 
   // Epilogue 2: the first LPR lanes of each 16-lane row hold distinct element
   // slices; they store the row's sums, and after one barrier each output
-  // thread folds the 8 waves x 4 rows itself (weights computed in place) and
-  // publishes this workgroup's partial device-wide.
-  constexpr int NWR = kWavesPerGroup * kRows16;
-  __shared__ float s_o[NWR][G][D];
-  __shared__ float s_m[NWR][G];
-  __shared__ float s_l[NWR][G];
-  __shared__ int32_t s_last;
+  // thread adds the 8 waves x 4 rows and publishes this workgroup's partial
+  // device-wide.
   const int wr = wave * kRows16 + (lane >> 4);
   if ((lane & 15) < LPR) {
 #pragma unroll
@@ -755,34 +767,33 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int c = 0; c < EPV; c += 4)
-          *reinterpret_cast<float4*>(&s_o[wr][h][(j * LPR + sub) * EPV + c]) =
+          *reinterpret_cast<float4*>(&s_o[wr][h * D + (j * LPR + sub) * EPV + c]) =
               make_float4(o[h][j * EPV + c], o[h][j * EPV + c + 1], o[h][j * EPV + c + 2], o[h][j * EPV + c + 3]);
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s_m[wr][h] = m_run[h];
-        s_l[wr][h] = l_acc[h];
-      }
-    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
+  // TPO adjacent threads share an output and add NWR / TPO rows each.
+  constexpr int TPO = G * D >= kGroupThreads ? 1 : (kGroupThreads / (G * D) >= 4 ? 4 : kGroupThreads / (G * D));
+  static_assert(TPO == 1 || TPO == 2 || TPO == 4, "threads per output");
+  for (int idx = threadIdx.x; idx < G * D * TPO; idx += kGroupThreads) {
+    const int out_i = idx / TPO, part = idx % TPO;
+    const int h = out_i / D, e = out_i % D;
+    float acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < NWR; ++r) M = fmaxf(M, s_m[r][h]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < NWR; ++r) {
-      const float mr = s_m[r][h];
-      const float w = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
-      acc = fmaf(w, s_o[r][h][e], acc);
-      lsum = fmaf(w, s_l[r][h], lsum);
-    }
+    for (int r = 0; r < NWR / TPO; ++r) acc += s_o[part * (NWR / TPO) + r][out_i];
+    if constexpr (TPO >= 2) acc += xor_lane<1>(acc);
+    if constexpr (TPO >= 4) acc += xor_lane<2>(acc);
+    if (part != 0) continue;
     const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
     publish(P.part_o + row * D + e, acc);
     if (e == 0) {
-      publish(P.part_ml + row * 2 + 0, M);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerGroup; ++w) lsum += s_l[w][h];
+      float mh = M[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh)
+        if (hh == h) mh = M[hh];
+      publish(P.part_ml + row * 2 + 0, mh);
       publish(P.part_ml + row * 2 + 1, lsum);
     }
   }
@@ -799,7 +810,31 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     s_last = prev == used - 1;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last) {
+    if constexpr (SRC == kSrcRing) {
+      if (P.pf_k != nullptr) {
+        // Warm L2 with the next layer's ring rows of this workgroup's tiles.
+        const char* pk = static_cast<const char*>(P.pf_k) + ((int64_t)b * P.Hkv + g) * P.pf_slots * D * ES;
+        const char* pv = static_cast<const char*>(P.pf_v) + ((int64_t)b * P.Hkv + g) * P.pf_slots * D * ES;
+        uint32_t sink = 0;
+        for (int32_t tile = tile_begin; tile < tile_end; ++tile) {
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
+            if (row < P.pf_slots) {
+#pragma unroll
+              for (int j = 0; j < NV; ++j) {
+                const int64_t off = (int64_t)row * D * ES + (j * LPR + sub) * 16;
+                sink ^= reinterpret_cast<const uint4*>(pk + off)->x ^ reinterpret_cast<const uint4*>(pv + off)->x;
+              }
+            }
+          }
+        }
+        asm volatile("" ::"v"(sink));
+      }
+    }
+    return;
+  }
   merge_and_write<DT, D, G>(P, b, g, used);
   if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[(int64_t)b * P.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
