@@ -6,11 +6,15 @@ batch 1, 131072-token prefilled context, s = 4, w = 2048, paged blocks of 16,
 recall scores drawn so exactly 12.5% of the timed steps fire.  One step is
 the whole hot path -- Local pass of every layer, device gate, gated Full pass
 of every layer, fused commit -- replayed from a captured HIP graph.
+--config selects another of the five workloads for an extra measurement line
+(1: 16K context, 3: 32 requests of mixed length, 4: hybrid sliding/gated
+layers with a focus region).
 
 Prints one JSON line: steps/s (value), effective KV GB/s and its share of
-HBM peak, the roofline of the dominant kernel (the Full-pass attention kernel,
-timed with HIP events on its launch stream), and the CPU oracle timed on a
-bounded sample as a reported baseline.
+HBM peak and of a plain device copy measured in the same run, the roofline of
+the dominant kernel (the Full-pass attention kernel, timed with HIP events on
+its launch stream), and the CPU oracle timed on a bounded sample as a
+reported baseline.
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,6 +34,7 @@ TRAFFIC_FILE = {"bf16": os.path.join(ROOT, "profiles", "traffic_full_attention_c
                 "fp8": os.path.join(ROOT, "profiles", "traffic_full_attention_ctx128k_fp8.json")}
 DTYPE_LABEL = {"bf16": "bf16", "fp8": "fp8_e4m3 K/V, bf16 q"}
 KERNEL_SRC = os.path.join(ROOT, "gated_kv_access_amd", "csrc", "oda_kernels.hip")
+METRIC = "decode steps/s and effective KV GB/s (% HBM peak) at 128K ctx, rho=0.125"
 
 
 def log(msg: str) -> None:
@@ -38,11 +44,17 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 1024, or the workload's)")
     ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", type=int, default=2, choices=(1, 2, 3, 4),
+                    help="workload: 1 16K, 2 128K (headline), 3 batched mixed, 4 hybrid + focus")
+    ap.add_argument("--focus", type=int, default=None, choices=(0, 1),
+                    help="workload 4: a fired gated layer reads the focus set (1, default) or all positions (0)")
     ap.add_argument("--rho", type=float, default=None, help="override the Full-call rate")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache storage: bf16, or FP8 E4M3 codes with per-tensor scales")
+    ap.add_argument("--reps", type=int, default=1,
+                    help="timed repetitions of the K steps from the same state (value: the median)")
     ap.add_argument("--roofline-launches", type=int, default=56)
     ap.add_argument("--sweep", action="store_true",
                     help="also time rho=0, rho=1 and always-Full for the savings check")
@@ -53,29 +65,50 @@ def parse():
     return ap.parse_args()
 
 
-def calibrate_copy() -> int:
-    """A plain copy kernel of known size: 1 GiB read and 1 GiB written per launch."""
+def copy_rate(n: int = 1 << 30, launches: int = 8):
+    """A plain device copy of n bytes: returns (us per launch, read+write GB/s)."""
     import torch
-    n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(8):
+    for _ in range(launches):
         dst.copy_(src)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 8
+    ms = e0.elapsed_time(e1) / launches
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms * 1e3, 2 * n / (ms * 1e-3) / 1e9
+
+
+def calibrate_copy() -> int:
+    n = 1 << 30
+    us, gbps = copy_rate(n)
     print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
-                      "launches": 8, "us_per_launch": round(ms * 1e3, 2),
-                      "gbps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+                      "launches": 8, "us_per_launch": round(us, 2), "gbps_read_plus_write": round(gbps, 1)}),
+          flush=True)
     return 0
 
 
 def kernel_sha() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def build_workload(args):
+    from gated_kv_access_amd import workloads as W
+    base = W.config(args.config)
+    if args.config == 4 and args.focus is not None:
+        base = base.with_(focus=bool(args.focus))
+    if args.kv_dtype == "fp8":
+        base = base.fp8()
+    if args.rho is not None:
+        base = base.with_(rho=(args.rho,))
+    K = args.steps if args.steps is not None else (1024 if args.config == 2 else base.steps)
+    return base, K
 
 
 def main() -> int:
@@ -96,11 +129,18 @@ def main() -> int:
     from gated_kv_access_amd.state import DecodeState
 
     B.load()
-    K, Wm = args.steps, args.warmup
-    base = W.config(2) if args.kv_dtype == "bf16" else W.config(2).fp8()
-    rho = base.rho[0] if args.rho is None else args.rho
-    wl = base.with_(steps=Wm + K, rho=(rho,))
-    log(f"workload {wl.name}: prefill {wl.prefill[0]}, warmup {Wm}, timed {K}, rho {rho}")
+    base, K = build_workload(args)
+    Wm = args.warmup
+    wl = base.with_(steps=Wm + K)
+    pre = np.array(wl.prefill, dtype=np.int64)
+    log(f"workload {wl.name}: batch {wl.batch}, prefill {pre.min()}..{pre.max()}, warmup {Wm}, timed {K}, "
+        f"rho {wl.rho if len(wl.rho) < 5 else 'per request'}")
+    if args.config == 3:
+        free = torch.cuda.mem_get_info()[0]
+        need = float((pre + Wm + K).sum()) * wl.num_layers * wl.num_kv_heads * wl.head_dim * 2 * wl.esize
+        if need > 0.92 * free:
+            log(f"paged cache of {need / 1e9:.0f} GB does not fit the {free / 1e9:.0f} GB free")
+            return 1
     t0 = time.time()
     st = DecodeState(wl, gen_device="cuda")
     st.prefill()
@@ -109,79 +149,62 @@ def main() -> int:
     sc = np.concatenate([W.gen_scores(wl.with_(steps=Wm)), W.gen_scores(wl.with_(steps=K))], 0) \
         if Wm > 0 else W.gen_scores(wl.with_(steps=K))
     scores = torch.from_numpy(sc).cuda()
-    log(f"setup {time.time() - t0:.1f}s (prefill of {wl.num_layers} layers x {wl.prefill[0]} positions)")
+    log(f"setup {time.time() - t0:.1f}s")
 
     r = StepRunner(st, q, k_new, v_new, scores, want_lse=False)
     r.capture()
     r.replay(Wm)
     torch.cuda.synchronize()
-    acct0 = r.counters.clone()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    r.replay(K)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    start_len = st.seq_len.clone()
+
+    def restore():
+        st.seq_len.copy_(start_len)
+        B.ring_init(st.dims, st.kv, wl.batch, st.workspace)  # ring state of the restored context
+        r.step_counter[0] = Wm
+        torch.cuda.synchronize()
+
+    times = []
+    acct = None
+    for rep in range(max(1, args.reps)):
+        if rep:
+            restore()
+        acct0 = r.counters.clone()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        r.replay(K)
+        end.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
+        if acct is None:
+            acct = (r.counters - acct0).cpu().numpy().sum(0)
     if st.device_error() != 0:
         log(f"device error word {st.device_error()}")
         return 1
-    acct = (r.counters - acct0).cpu().numpy()[0]
+    ms = statistics.median(times)
     f = dict(zip(B.ACCT_FIELDS, acct.tolist()))
     steps_per_s = K / (ms / 1e3)
     kv_gbps = f["kv_bytes"] / (ms / 1e3) / 1e9
-    log(f"timed {K} steps in {ms:.1f} ms: {steps_per_s:.1f} steps/s, {kv_gbps:.0f} GB/s effective KV, "
-        f"{f['full_calls']} Full calls")
+    log(f"timed {K} steps in {ms:.1f} ms (median of {len(times)}): {steps_per_s:.1f} steps/s, "
+        f"{kv_gbps:.0f} GB/s effective KV, {f['full_calls']} Full calls")
 
-    # ---------------------------------------------------------------- roofline leg
-    # The dominant kernel: the Full-pass attention kernel (split-K over the paged
-    # cache + last-workgroup merge), one launch per oda_decode_full_gated call,
-    # every call firing.  Timed over all its launches with HIP events on the stream
-    # the launches go to (torch's current stream).
-    L, Hkv, d = wl.num_layers, wl.num_kv_heads, wl.head_dim
-    t_now = int(st.seq_len[0].item()) + 1
-    fire = torch.ones(4, dtype=torch.float32, device="cuda")
-    out = torch.empty((1, wl.num_q_heads, d), dtype=torch.float32, device="cuda")
-    qs = [q[-1, l].contiguous() for l in range(L)]
-    ks = [k_new[-1, l].contiguous() for l in range(L)]
-    vs = [v_new[-1, l].contiguous() for l in range(L)]
-    R = args.roofline_launches
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(R):
-        l = i % L
-        B.decode_full_gated(st.dims, st.kv, l, 1, qs[l], ks[l], vs[l], fire, 0.0, out, None, None, None,
-                            st.workspace)
-    e1.record()
-    torch.cuda.synchronize()
-    avg_us = e0.elapsed_time(e1) * 1e3 / R
-    bytes_per_launch = (t_now - 1) * Hkv * d * 2 * wl.esize  # K and V rows streamed from the paged cache
-    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE[args.kv_dtype]):
-        with open(TRAFFIC_FILE[args.kv_dtype]) as fh:
-            tr = json.load(fh)
-        if tr.get("kernel_sha") == kernel_sha():
-            traffic = tr.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": f"attention_kernel<{args.kv_dtype},128,G2,paged,ballot>", "avg_launch_us": round(avg_us, 2),
-                "bytes_per_launch": bytes_per_launch, "launches": R}
-    log(f"roofline: Full-pass kernel {avg_us:.1f} us/launch, {achieved:.0f} GB/s = "
-        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak")
+    roofline = roofline_leg(args, st, wl, q, k_new, v_new)
+    copy_us, copy_gbps = copy_rate()
+    log(f"device copy reference: {copy_gbps:.0f} GB/s read+write")
 
     extra = {}
     if args.sweep:
-        extra = sweep(st, wl, q, k_new, v_new, K, Wm, log)
+        extra = sweep(st, wl, q, k_new, v_new, K, Wm, start_len)
 
-    # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(st, wl, q, rho, args.cpu_layers, log)
+        if wl.batch == 1 and not wl.sliding_layers:
+            cpu = cpu_baseline(st, wl, q, float(wl.rho[0]), args.cpu_layers)
+        else:
+            log("cpu baseline: timed on the single-request workloads only")
 
     res = {
-        "metric": "decode steps/s and effective KV GB/s (% HBM peak) at 128K ctx, rho=0.125",
+        "metric": METRIC,
         "value": round(steps_per_s, 2),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -193,37 +216,98 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": DTYPE_LABEL[args.kv_dtype],
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": L, "q_heads": wl.num_q_heads, "kv_heads": Hkv,
-                   "head_dim": d, "batch": wl.batch, "prefill": wl.prefill[0], "sink": wl.sink,
-                   "window": wl.window, "block_size": wl.block_size, "rho": rho, "kv_dtype": wl.dtype,
+        "config": {"workload": wl.name, "layers": wl.num_layers, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "batch": wl.batch,
+                   "prefill": int(pre[0]) if wl.batch == 1 else [int(pre.min()), int(pre.max())],
+                   "sink": wl.sink, "window": wl.window, "block_size": wl.block_size,
+                   "rho": list(wl.rho) if len(wl.rho) > 1 else wl.rho[0], "kv_dtype": wl.dtype,
+                   "sliding_layers": len(wl.sliding_layers), "focus": bool(wl.focus),
                    "full_calls_timed": int(f["full_calls"]), "parallelism": "single GPU"},
         "tokens_per_s": round(steps_per_s * wl.batch, 2),
         "effective_kv_gbps": round(kv_gbps, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "device_copy_gbps": round(copy_gbps, 1),
+        "pct_device_copy": round(100 * kv_gbps / copy_gbps, 2),
         "flops_ratio_vs_full": round((f["f_local"] + f["f_full_taken"] + f["f_recall"]) / f["f_full_always"], 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if len(times) > 1:
+        res["ms_per_rep"] = [round(t, 3) for t in times]
     res.update(extra)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def sweep(st, wl, q, k_new, v_new, K, Wm, log):
+def roofline_leg(args, st, wl, q, k_new, v_new):
+    """The dominant kernel: the Full-pass attention kernel (split-K over the paged
+    cache + last-workgroup merge), one launch per oda_decode_full_gated call on a
+    gated layer, every request firing.  Timed over all its launches with HIP
+    events on the stream the launches go to (torch's current stream)."""
+    import torch
+
+    from gated_kv_access_amd import binding as B
+
+    Bn, Hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    gated = list(wl.gated_layers)
+    fire = torch.ones(max(4, Bn + (-Bn) % 4), dtype=torch.float32, device="cuda")
+    out = torch.empty((Bn, wl.num_q_heads, d), dtype=torch.float32, device="cuda")
+    # rows each launch streams from the paged cache: the library's own Full set, minus t
+    cap = max(wl.rows(b) for b in range(Bn)) + 8
+    pos = torch.empty(cap, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rows = 0
+    for b in range(Bn):
+        B.access_set(st.dims, st.kv, gated[0], b, 1, pos, cnt, st.workspace)
+        rows += int(cnt.item()) - 1
+    bytes_per_launch = rows * Hkv * d * 2 * wl.esize  # K and V rows streamed from the paged cache
+    qs = [q[-1, l].contiguous() for l in gated]
+    ks = [k_new[-1, l].contiguous() for l in gated]
+    vs = [v_new[-1, l].contiguous() for l in gated]
+    R = args.roofline_launches
+    for i in range(len(gated)):
+        B.decode_full_gated(st.dims, st.kv, gated[i], Bn, qs[i], ks[i], vs[i], fire, 0.0, out, None, None, None,
+                            st.workspace)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(R):
+        j = i % len(gated)
+        B.decode_full_gated(st.dims, st.kv, gated[j], Bn, qs[j], ks[j], vs[j], fire, 0.0, out, None, None, None,
+                            st.workspace)
+    e1.record()
+    torch.cuda.synchronize()
+    avg_us = e0.elapsed_time(e1) * 1e3 / R
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    traffic = None
+    tf = TRAFFIC_FILE[args.kv_dtype]
+    if args.config == 2 and os.path.exists(tf):
+        with open(tf) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_sha") == kernel_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+    log(f"roofline: Full-pass kernel {avg_us:.1f} us/launch, {achieved:.0f} GB/s = "
+        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak")
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": f"attention_kernel<{args.kv_dtype},{d},G{wl.num_q_heads // Hkv},paged,ballot>",
+            "avg_launch_us": round(avg_us, 2), "bytes_per_launch": bytes_per_launch, "launches": R}
+
+
+def sweep(st, wl, q, k_new, v_new, K, Wm, start_len):
     """rho = 0, rho = 1 and always-Full over the same K steps, for the step-time
     ratio against the FLOP prediction of the per-step savings equation."""
-    import numpy as np
     import torch
 
     from gated_kv_access_amd import binding as B
     from gated_kv_access_amd.runner import StepRunner
 
-    P = wl.prefill[0]
+    Bn = wl.batch
     out = {}
 
     def time_runner(r, label):
-        st.seq_len.fill_(P + Wm)
-        B.ring_init(st.dims, st.kv, 1, st.workspace)  # ring state of the reset context
+        st.seq_len.copy_(start_len)
+        B.ring_init(st.dims, st.kv, Bn, st.workspace)  # ring state of the reset context
         r.capture()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -236,14 +320,14 @@ def sweep(st, wl, q, k_new, v_new, K, Wm, log):
         return ms / K
 
     for label, val in (("rho0", -1.0), ("rho1", 1.0)):
-        sc = torch.full((Wm + K, 1), val, dtype=torch.float32, device="cuda")
+        sc = torch.full((Wm + K, Bn), val, dtype=torch.float32, device="cuda")
         r = StepRunner(st, q, k_new, v_new, sc, want_lse=False)
         r.step_counter[0] = Wm
         out[f"us_per_step_{label}"] = round(time_runner(r, label) * 1e3, 2)
     # Always-Full: every layer's Full pass and the commit, no Local attempt, no gate.
-    fire = torch.ones(4, dtype=torch.float32, device="cuda")
+    fire = torch.ones(max(4, Bn + (-Bn) % 4), dtype=torch.float32, device="cuda")
     L = wl.num_layers
-    o = torch.empty((L, 1, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    o = torch.empty((L, Bn, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
     ctr = torch.tensor([Wm, 0], dtype=torch.int64, device="cuda")
     qb, kb, vb = torch.empty_like(q[0]), torch.empty_like(k_new[0]), torch.empty_like(v_new[0])
 
@@ -256,9 +340,9 @@ def sweep(st, wl, q, k_new, v_new, K, Wm, log):
                 with torch.cuda.graph(g, stream=s):
                     B.stage_step([q, k_new, v_new], [qb, kb, vb], ctr, q.shape[0])
                     for l in range(L):
-                        B.decode_full_gated(st.dims, st.kv, l, 1, qb[l], kb[l], vb[l], fire, 0.0, o[l], None,
+                        B.decode_full_gated(st.dims, st.kv, l, Bn, qb[l], kb[l], vb[l], fire, 0.0, o[l], None,
                                             None, None, st.workspace)
-                    B.commit_kv(st.dims, st.kv, 1, kb, vb, st.workspace)
+                    B.commit_kv(st.dims, st.kv, Bn, kb, vb, st.workspace)
             torch.cuda.current_stream().wait_stream(s)
             self.g = g
 
@@ -268,14 +352,14 @@ def sweep(st, wl, q, k_new, v_new, K, Wm, log):
 
     ms_full = time_runner(FullOnly(), "always-Full")
     out["us_per_step_full_only"] = round(ms_full * 1e3, 2)
-    st.seq_len.fill_(P + Wm + K)
     return {"sweep": out}
 
 
-def cpu_baseline(st, wl, q, rho, n_layers, log):
-    """The fp64 oracle on the host cores over a bounded sample: n_layers of the 28
+def cpu_baseline(st, wl, q, rho, n_layers):
+    """The fp64 oracle on the host cores over a bounded sample: n_layers of the
     layers, 2 Local-only and 2 fired steps at the end of the timed context,
-    scaled linearly to all layers and combined as T(rho) = (1-rho) T_L + rho T_F."""
+    scaled linearly to all layers and combined as T(rho) = (1-rho) T_L + rho T_F;
+    then the same with one thread on one layer and one step of each kind."""
     import numpy as np
     import torch
 
@@ -283,36 +367,45 @@ def cpu_baseline(st, wl, q, rho, n_layers, log):
     from gated_kv_access_amd import workloads as W
 
     t_end = int(st.seq_len[0].item())  # positions committed by the end of the run
-    k = 2
-    P0 = t_end - k
-    layers = list(range(n_layers))
-    rows = t_end
     fp8 = wl.dtype == "fp8"
     kv_words = (lambda x: x.view(torch.uint8).cpu().numpy()) if fp8 else \
         (lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16))
-    ks = np.zeros((n_layers, 1, rows, wl.num_kv_heads, wl.head_dim), np.uint8 if fp8 else np.uint16)
+    ks = np.zeros((n_layers, 1, t_end, wl.num_kv_heads, wl.head_dim), np.uint8 if fp8 else np.uint16)
     vs = np.zeros_like(ks)
-    for i, l in enumerate(layers):
-        ks[i, 0] = kv_words(W.gen_sequence(wl, l, 0, "k", "cuda")[:rows])
-        vs[i, 0] = kv_words(W.gen_sequence(wl, l, 0, "v", "cuda")[:rows])
-    qq = q[:k, :n_layers].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    cfg = orc.OracleConfig(n_layers, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, sink=wl.sink,
-                           window=wl.window, dtype=orc.FP8 if fp8 else orc.BF16,
-                           k_scale=wl.k_scale, v_scale=wl.v_scale)
+    for l in range(n_layers):
+        ks[l, 0] = kv_words(W.gen_sequence(wl, l, 0, "k", "cuda")[:t_end])
+        vs[l, 0] = kv_words(W.gen_sequence(wl, l, 0, "v", "cuda")[:t_end])
+    qq = q[:2, :n_layers].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def run(layers, k, threads):
+        orc.set_threads(threads)
+        cfg = orc.OracleConfig(layers, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, sink=wl.sink,
+                               window=wl.window, dtype=orc.FP8 if fp8 else orc.BF16,
+                               k_scale=wl.k_scale, v_scale=wl.v_scale)
+        tm = {}
+        for label, val in (("local", -1.0), ("full", 1.0)):
+            s = np.full((k, 1), val, np.float32)
+            t0 = time.perf_counter()
+            orc.decode_run(cfg, [t_end - k], ks[:layers], vs[:layers],
+                           np.ascontiguousarray(qq[:k, :layers]), s)
+            tm[label] = (time.perf_counter() - t0) / k * (wl.num_layers / layers)
+        return tm
+
     threads = orc.get_threads()
-    times = {}
-    for label, val in (("local", -1.0), ("full", 1.0)):
-        sc = np.full((k, 1), val, np.float32)
-        t0 = time.perf_counter()
-        orc.decode_run(cfg, [P0], ks, vs, qq, sc)
-        times[label] = (time.perf_counter() - t0) / k * (wl.num_layers / n_layers)
-    t_step = (1 - rho) * times["local"] + rho * times["full"]
-    log(f"cpu oracle ({threads} threads): Local step {times['local']:.3f}s, Full step {times['full']:.3f}s "
+    tm = run(n_layers, 2, threads)
+    t_step = (1 - rho) * tm["local"] + rho * tm["full"]
+    log(f"cpu oracle ({threads} threads): Local step {tm['local']:.3f}s, Full step {tm['full']:.3f}s "
         f"(scaled to {wl.num_layers} layers)")
+    tm1 = run(1, 1, 1)
+    orc.set_threads(threads)
+    t1 = (1 - rho) * tm1["local"] + rho * tm1["full"]
+    log(f"cpu oracle (1 thread): Local step {tm1['local']:.3f}s, Full step {tm1['full']:.3f}s")
     return {"value": round(1.0 / t_step, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_layers} of {wl.num_layers} layers, {k} Local-only + {k} fired steps at "
-                      f"t={P0 + 1}..{t_end}, scaled linearly to all layers, "
-                      f"T(rho)=(1-rho)T_L+rho*T_F with rho={rho}"}
+            "sample": f"{n_layers} of {wl.num_layers} layers, 2 Local-only + 2 fired steps at "
+                      f"t={t_end - 1}..{t_end}, scaled linearly to all layers, "
+                      f"T(rho)=(1-rho)T_L+rho*T_F with rho={rho}",
+            "value_1thread": round(1.0 / t1, 5),
+            "sample_1thread": f"1 layer, 1 Local-only + 1 fired step at t={t_end}, 1 thread, same scaling"}
 
 
 if __name__ == "__main__":

@@ -106,15 +106,23 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     if (f > tiles) f = tiles;
     if (f > kMaxSplits) f = kMaxSplits;
     p->full_splits = f < 1 ? 1 : f;
+    // Ring passes: one tile per workgroup while the (request, KV head) pairs
+    // leave the chip unfilled; at larger batches a single round of workgroups,
+    // each taking several tiles, so that no workgroup's fixed cost is paid twice
+    // per CU.
     const int32_t rtiles = ceil_div(p->ring_slots + 1, tile);
-    int32_t l = d->local_splits > 0 ? d->local_splits : rtiles;  // one tile per workgroup
+    const int64_t pairs = (int64_t)b * p->Hkv;
+    const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
+    int32_t l = d->local_splits > 0 ? d->local_splits : round;
     if (l > rtiles) l = rtiles;
     if (l > kMaxSplits) l = kMaxSplits;
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
     const int32_t stiles = ceil_div(p->sw_window + 1, tile);
-    int32_t s = d->local_splits > 0 ? d->local_splits : stiles;
+    const int64_t pairs = (int64_t)b * p->Hkv;
+    const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
+    int32_t s = d->local_splits > 0 ? d->local_splits : round;
     if (s > stiles) s = stiles;
     if (s > kMaxSplits) s = kMaxSplits;
     p->sw_splits = s < 1 ? 1 : s;
