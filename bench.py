@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--rho", type=float, default=None, help="override the Full-call rate")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache storage: bf16, or FP8 E4M3 codes with per-tensor scales")
+    ap.add_argument("--host-kv", action="store_true",
+                    help="paged history in pinned host memory (rings in HBM); the Full pass reads it over the host link")
     ap.add_argument("--reps", type=int, default=1,
                     help="timed repetitions of the K steps from the same state (value: the median)")
     ap.add_argument("--roofline-launches", type=int, default=56)
@@ -82,6 +84,24 @@ def copy_rate(n: int = 1 << 30, launches: int = 8):
     del src, dst
     torch.cuda.empty_cache()
     return ms * 1e3, 2 * n / (ms * 1e-3) / 1e9
+
+
+def host_copy_rate(n: int = 1 << 30, launches: int = 4) -> float:
+    """Pinned host to device copy of n bytes (DMA): GB/s."""
+    import torch
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    del src, dst
+    return n / (ms * 1e-3) / 1e9
 
 
 def calibrate_copy() -> int:
@@ -142,7 +162,7 @@ def main() -> int:
             log(f"paged cache of {need / 1e9:.0f} GB does not fit the {free / 1e9:.0f} GB free")
             return 1
     t0 = time.time()
-    st = DecodeState(wl, gen_device="cuda")
+    st = DecodeState(wl, gen_device="cuda", host_cache=args.host_kv)
     st.prefill()
     q = W.gen_queries(wl, "cuda")
     k_new, v_new = st.decode_inputs()
@@ -191,6 +211,13 @@ def main() -> int:
     roofline = roofline_leg(args, st, wl, q, k_new, v_new)
     copy_us, copy_gbps = copy_rate()
     log(f"device copy reference: {copy_gbps:.0f} GB/s read+write")
+    host_gbps = None
+    if args.host_kv:
+        host_gbps = host_copy_rate()
+        log(f"host-to-device DMA reference: {host_gbps:.1f} GB/s")
+        roofline["bound"] = "host_link"
+        roofline["host_dma_gbps"] = round(host_gbps, 1)
+        roofline["frac_of_host_dma"] = round(roofline["achieved"] / host_gbps, 4)
 
     extra = {}
     if args.sweep:
@@ -222,6 +249,7 @@ def main() -> int:
                    "sink": wl.sink, "window": wl.window, "block_size": wl.block_size,
                    "rho": list(wl.rho) if len(wl.rho) > 1 else wl.rho[0], "kv_dtype": wl.dtype,
                    "sliding_layers": len(wl.sliding_layers), "focus": bool(wl.focus),
+                   "paged_history": "pinned host memory" if args.host_kv else "HBM",
                    "full_calls_timed": int(f["full_calls"]), "parallelism": "single GPU"},
         "tokens_per_s": round(steps_per_s * wl.batch, 2),
         "effective_kv_gbps": round(kv_gbps, 1),

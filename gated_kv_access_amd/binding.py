@@ -26,7 +26,8 @@ DEVERR_CAPACITY, DEVERR_BLOCK_ID, DEVERR_OUT_CAPACITY = 1, 2, 4
 # Every symbol include/oda.h declares.
 EXPORTS = ("oda_workspace_size", "oda_workspace_init", "oda_prefill_kv", "oda_ring_init",
            "oda_commit_kv", "oda_decode_local", "oda_decode_full_gated", "oda_gate", "oda_step",
-           "oda_access_set", "oda_stage_step", "oda_advance_counter", "oda_status_string")
+           "oda_access_set", "oda_stage_step", "oda_advance_counter", "oda_host_kv_pointer",
+           "oda_status_string")
 
 
 class OdaError(RuntimeError):
@@ -87,6 +88,7 @@ def load(path: str = LIB_PATH):
         "oda_access_set": (I32, [D, K, I32, I32, I32, P, I64, P, P, SZ, P]),
         "oda_stage_step": (I32, [I32, P, P, P, P, I64, P]),
         "oda_advance_counter": (I32, [P, P]),
+        "oda_host_kv_pointer": (I32, [P, ctypes.POINTER(ctypes.c_void_p)]),
         "oda_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sig.items():
@@ -197,3 +199,10 @@ def stage_step(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor], step_
 
 def advance_counter(step_counter: torch.Tensor, stream=None) -> None:
     _check("oda_advance_counter", load().oda_advance_counter(_p(step_counter), _stream(stream)))
+
+
+def host_kv_pointer(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor (for host-resident paged caches)."""
+    out = ctypes.c_void_p()
+    _check("oda_host_kv_pointer", load().oda_host_kv_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)))
+    return out.value

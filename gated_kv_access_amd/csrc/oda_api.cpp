@@ -436,6 +436,12 @@ oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream) {
   return hip_status(oda::launch_advance(step_counter, stream));
 }
 
+oda_status oda_host_kv_pointer(void* host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr) return ODA_ERR_INVALID_ARG;
+  const int rc = oda::host_device_pointer(host_ptr, device_ptr);
+  return rc == 0 ? ODA_OK : (rc == 1 ? ODA_ERR_INVALID_ARG : ODA_ERR_HIP);
+}
+
 const char* oda_status_string(oda_status status) {
   switch (status) {
     case ODA_OK: return "ODA_OK";

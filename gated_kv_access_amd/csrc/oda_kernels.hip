@@ -1480,4 +1480,20 @@ int launch_advance(int64_t* counter, oda_stream s) {
   return (int)hipGetLastError();
 }
 
+int host_device_pointer(void* host_ptr, void** device_ptr) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host_ptr) != hipSuccess) {
+    (void)hipGetLastError();  // an unknown pointer leaves an error behind: clear it
+    return 1;
+  }
+  if (attr.type != hipMemoryTypeHost) return 1;
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, host_ptr, 0) != hipSuccess || dev == nullptr) {
+    (void)hipGetLastError();
+    return 2;
+  }
+  *device_ptr = dev;
+  return 0;
+}
+
 }  // namespace oda

@@ -22,6 +22,13 @@ def _raw(x: torch.Tensor) -> torch.Tensor:
     return x.view(torch.uint8) if x.dtype == torch.float8_e4m3fn else x
 
 
+def _raw_fill(fill: float, dt: torch.dtype):
+    """The fill value as the raw element of a host buffer filled through _raw()."""
+    if dt == torch.float8_e4m3fn:
+        return int(torch.tensor([fill]).to(dt).view(torch.uint8).item())
+    return fill
+
+
 def make_dims(wl: Workload, full_splits: int = 0, local_splits: int = 0,
               focus: Optional[bool] = None, recall_flops: int = 0) -> B.OdaDims:
     d = B.OdaDims()
@@ -54,7 +61,8 @@ class DecodeState:
     """All device buffers of a run sized for workload `wl`."""
 
     def __init__(self, wl: Workload, device="cuda", dims: Optional[B.OdaDims] = None,
-                 spare_blocks: int = 0, fill: float = float("nan"), gen_device=None):
+                 spare_blocks: int = 0, fill: float = float("nan"), gen_device=None,
+                 host_cache: bool = False):
         self.wl = wl
         self.device = torch.device(device)
         # Where the seeded generator draws: the device itself (fast), or "cpu" so
@@ -68,8 +76,18 @@ class DecodeState:
         self.num_blocks = nblocks
         self.block_table = torch.from_numpy(table).to(self.device)
         R = wl.sink + wl.window
-        self.k_cache = torch.full((Lg, nblocks, Hkv, wl.block_size, d), fill, dtype=dt, device=self.device) if Lg else None
-        self.v_cache = torch.full_like(self.k_cache, fill) if Lg else None
+        # host_cache: the paged history in pinned host memory (read by the Full
+        # pass over the host link); the rings stay in HBM.
+        self.host_cache = host_cache
+        if Lg and host_cache:
+            shape = (Lg, nblocks, Hkv, wl.block_size, d)
+            self.k_cache = torch.empty(shape, dtype=dt, pin_memory=True)
+            self.v_cache = torch.empty(shape, dtype=dt, pin_memory=True)
+            _raw(self.k_cache).view(-1).fill_(_raw_fill(fill, dt))
+            _raw(self.v_cache).view(-1).fill_(_raw_fill(fill, dt))
+        else:
+            self.k_cache = torch.full((Lg, nblocks, Hkv, wl.block_size, d), fill, dtype=dt, device=self.device) if Lg else None
+            self.v_cache = torch.full_like(self.k_cache, fill) if Lg else None
         self.k_ring = torch.full((Lg, Bn, Hkv, R, d), fill, dtype=dt, device=self.device) if Lg else None
         self.v_ring = torch.full_like(self.k_ring, fill) if Lg else None
         self.ring_pos = torch.full((Bn, R), -7, dtype=torch.int32, device=self.device) if Lg else None
@@ -85,8 +103,12 @@ class DecodeState:
         self.workspace = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.kv = B.OdaKV()
         kv = self.kv
-        kv.k_cache = B._p(self.k_cache) if Lg else None
-        kv.v_cache = B._p(self.v_cache) if Lg else None
+        if Lg and host_cache:
+            kv.k_cache = B.host_kv_pointer(self.k_cache)
+            kv.v_cache = B.host_kv_pointer(self.v_cache)
+        else:
+            kv.k_cache = B._p(self.k_cache) if Lg else None
+            kv.v_cache = B._p(self.v_cache) if Lg else None
         kv.k_ring = B._p(self.k_ring) if Lg else None
         kv.v_ring = B._p(self.v_ring) if Lg else None
         kv.k_swring = B._p(self.k_swring) if Ls else None

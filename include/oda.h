@@ -235,6 +235,17 @@ oda_status oda_stage_step(int32_t n, const void* const* src, void* const* dst,
 /* step_counter[0] += 1 (one tiny kernel). */
 oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream);
 
+/* Host.  Host-resident paged history (zhichai.net Declarative Attention page,
+ * section "System-2 KV Cache Offloading": KV that the local mode does not
+ * need may live in CPU memory and be read only when global attention is
+ * declared).  The paged caches of oda_kv may be pinned host memory: only the
+ * rings must be in HBM, and the Full pass then reads the history over the host
+ * link, only for the requests whose gate fired.  Given a pointer into pinned
+ * host memory (hipHostMalloc, or a pinned torch tensor), writes the address at
+ * which kernels reach it to *device_ptr; ODA_ERR_INVALID_ARG if the memory is
+ * not pinned host memory, ODA_ERR_HIP if the runtime call fails. */
+oda_status oda_host_kv_pointer(void* host_ptr, void** device_ptr);
+
 /* Host.  Human-readable status name. */
 const char* oda_status_string(oda_status status);
 

@@ -164,6 +164,9 @@ def test_helpers_reject_bad_arguments(lib):
     assert lib.oda_stage_step(1, arr, arr, by, FAKE, 4, None) == -1
     assert lib.oda_stage_step(0, arr, arr, by, FAKE, 4, None) == -1
     assert lib.oda_advance_counter(None, None) == -1
+    out = ctypes.c_void_p()
+    assert lib.oda_host_kv_pointer(None, ctypes.byref(out)) == -1
+    assert lib.oda_host_kv_pointer(FAKE, None) == -1
 
 
 def test_status_strings(lib):

@@ -25,10 +25,10 @@ pytestmark = pytest.mark.gpu
 _POOL = min(16, os.cpu_count() or 4)
 
 
-def _run_and_sample(wl, steps, sample_steps, sample_layers, sample_requests):
+def _run_and_sample(wl, steps, sample_steps, sample_layers, sample_requests, host_cache=False):
     wl = wl.with_(steps=steps)
     say(f"{wl.name}: batch {wl.batch}, {wl.num_layers} layers, max prefill {max(wl.prefill)}, {steps} steps")
-    st = DecodeState(wl, gen_device="cuda")
+    st = DecodeState(wl, gen_device="cuda", host_cache=host_cache)
     st.prefill()
     q = W.gen_queries(wl, "cuda")
     k_new, v_new = st.decode_inputs()
@@ -148,3 +148,12 @@ def test_hybrid_focus_fp8_kv_sampled():
     steps = 8
     out = _run_and_sample(wl, steps, {0, steps - 1}, (3, 31), (0, 7))
     _check(*out, (3, 31), (0, 7))
+
+
+def test_ctx128k_host_resident_history_sampled():
+    """The 128K workload with the paged history in pinned host memory: 4 steps,
+    two of them firing (Full passes read 15 GB over the host link)."""
+    wl = W.config(2).with_(score_mode="exact", rho=(0.5,))
+    steps = 4
+    out = _run_and_sample(wl, steps, {0, 1, 2, 3}, (0, 27), (0,), host_cache=True)
+    _check(*out, (0, 27), (0,))

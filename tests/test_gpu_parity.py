@@ -38,9 +38,9 @@ SMALL = [
 ]
 
 
-def _check_run(wl, graph=False, q_full=False):
-    say(f"{wl.name}: prefill {wl.prefill}, {wl.steps} steps, graph={graph}")
-    st = DecodeState(wl, gen_device="cpu")
+def _check_run(wl, graph=False, q_full=False, host_cache=False):
+    say(f"{wl.name}: prefill {wl.prefill}, {wl.steps} steps, graph={graph}, host_cache={host_cache}")
+    st = DecodeState(wl, gen_device="cpu", host_cache=host_cache)
     st.prefill()
     q = W.gen_queries(wl, "cpu")
     qf = W.gen_queries(wl, "cpu", tag=4) if q_full else None
@@ -322,3 +322,33 @@ def test_fp8_equals_bf16_path_on_the_same_values():
     diff = float(np.abs(r8.out - rb.out).max())
     say(f"fp8 vs bf16 path on identical values: max diff {diff:.3e}")
     assert diff <= 2e-5
+
+
+# ---------------------------------------------------------------- host-resident paged history
+
+HOST = [
+    _small("host_bf16_d128_g2", seed=141),
+    _small("host_fp8_d64_g1", head_dim=64, num_q_heads=2, num_kv_heads=2, seed=142).fp8(),
+    _small("host_hybrid_focus", num_layers=8, sw_window=64, sink=4, window=128, batch=3,
+           prefill=(1000, 2500, 6000), steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)),
+           focus=True, seed=143),
+]
+
+
+@pytest.mark.parametrize("wl", HOST, ids=[w.name for w in HOST])
+def test_host_resident_paged_history_matches_oracle(wl):
+    """Paged caches in pinned host memory (prefill, commit and Full pass reach
+    them over the host link), rings in HBM, replayed from a graph."""
+    _check_run(wl, host_cache=True, graph=True)
+
+
+def test_host_kv_pointer_rejects_device_and_pageable_memory():
+    dev = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    pageable = torch.empty(1024, dtype=torch.uint8)
+    for t in (dev, pageable):
+        with pytest.raises(B.OdaError) as e:
+            B.host_kv_pointer(t)
+        assert e.value.status == -1
+    pinned = torch.empty(1024, dtype=torch.uint8, pin_memory=True)
+    assert B.host_kv_pointer(pinned) != 0
+    torch.cuda.synchronize()
