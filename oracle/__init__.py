@@ -12,7 +12,10 @@ only marshals numpy arrays through ctypes.  Sources followed:
   q_t > theta with theta = 0;
 * same page, section "Computational Savings": the per-step savings equation;
 * the Declarative Attention pages ("Three Attention Modes"): focus reads one
-  contiguous region; sliding-window layers keep a fixed recent window.
+  contiguous region; sliding-window layers keep a fixed recent window;
+* the recall score q_t = R_psi(h_{t-1}, E(x_t), h^L_t) of "Local-First
+  Decoding", with a one-hidden-layer stand-in for R_psi (the pages give its
+  inputs and size, not its layers).
 """
 from __future__ import annotations
 
@@ -97,6 +100,8 @@ def _bind(path: str):
     L.oracle_attention.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double, P,
                                    ctypes.c_int64, P, P]
+    L.oracle_recall_head.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_float, P, ctypes.c_int32, P]
+    L.oracle_recall_head.restype = None
     L.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
     L.oracle_fp8_e4m3.restype = ctypes.c_double
     L.oracle_attention.restype = ctypes.c_double
@@ -245,6 +250,21 @@ def decode_run(cfg: OracleConfig, prefill: Sequence[int], kseq: np.ndarray, vseq
         raise ValueError("oracle_decode_run rejected its arguments")
     return dict(out=out, lse=lse, fire=fire, call_list=call_list, call_count=call_count,
                 full_calls=full_calls, acct=acct)
+
+
+def recall_head(w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: float, x: np.ndarray) -> np.ndarray:
+    """Recall scores q [batch] (float64) of the one-hidden-layer stand-in head.
+
+    w1: bf16 words [hidden][in_dim]; b1, w2: float32 [hidden]; x: bf16 words [batch][in_dim]."""
+    w1 = np.ascontiguousarray(w1, dtype=np.uint16)
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.uint16)
+    b1 = np.ascontiguousarray(b1, dtype=np.float32)
+    w2 = np.ascontiguousarray(w2, dtype=np.float32)
+    hidden, in_dim = w1.shape
+    assert x.shape[1] == in_dim and b1.shape == (hidden,) and w2.shape == (hidden,)
+    q = np.zeros(x.shape[0], dtype=np.float64)
+    lib().oracle_recall_head(in_dim, hidden, _ptr(w1), _ptr(b1), _ptr(w2), float(b2), _ptr(x), x.shape[0], _ptr(q))
+    return q
 
 
 def bf16_to_f64(w: np.ndarray) -> np.ndarray:

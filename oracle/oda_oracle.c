@@ -300,6 +300,30 @@ int oracle_decode_run(const oracle_cfg* c, int32_t B, int32_t K, const int64_t* 
   return 0;
 }
 
+/* Recall score of the recall head, q_t = R_psi(h_{t-1}, E(x_t), h^L_t) of
+ * "Local-First Decoding" (picx.dev summary).  The pages fix the inputs and the
+ * size of R_psi but not its layers; the stand-in is one hidden layer with
+ * ReLU: x = [h_{t-1}; E(x_t); h^L_t] (in_dim values), u = W1 x + b1
+ * (hidden values), q = w2 . max(u, 0) + b2.
+ *   w1 : bf16 words [hidden][in_dim];  b1, w2 : f32 [hidden];  b2 : f32
+ *   x  : bf16 words [batch][in_dim];   q  : double [batch]
+ * Plain fp64 loops; OpenMP only over independent requests. */
+void oracle_recall_head(int32_t in_dim, int32_t hidden, const uint16_t* w1, const float* b1,
+                        const float* w2, float b2, const uint16_t* x, int32_t batch, double* q) {
+#pragma omp parallel for schedule(static)
+  for (int32_t b = 0; b < batch; ++b) {
+    const uint16_t* xb = x + (int64_t)b * in_dim;
+    double acc = (double)b2;
+    for (int32_t j = 0; j < hidden; ++j) {
+      const uint16_t* row = w1 + (int64_t)j * in_dim;
+      double u = (double)b1[j];
+      for (int32_t i = 0; i < in_dim; ++i) u += widen(row, OR_BF16, i) * widen(xb, OR_BF16, i);
+      if (u > 0.0) acc += (double)w2[j] * u;
+    }
+    q[b] = acc;
+  }
+}
+
 void oracle_set_threads(int32_t n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);

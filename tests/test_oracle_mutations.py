@@ -40,6 +40,13 @@ MUTATIONS = [
     ("fp8_v_scale_dropped", "(v_scale * widen(kv_v, dtype, row + j))", "(widen(kv_v, dtype, row + j))",
      ["fp8_sdpa"]),
     ("fp8_query_read_as_fp8", "const int32_t qt = q_dtype(dtype);", "const int32_t qt = dtype;", ["fp8_sdpa"]),
+    ("head_no_relu", "if (u > 0.0) acc += (double)w2[j] * u;", "acc += (double)w2[j] * u;",
+     ["test_recall_head_worked_example"]),
+    ("head_no_b1", "double u = (double)b1[j];", "double u = 0.0;", ["test_recall_head_worked_example"]),
+    ("head_no_b2", "double acc = (double)b2;", "double acc = 0.0;", ["test_recall_head_worked_example"]),
+    ("head_w1_transposed", "u += widen(row, OR_BF16, i) * widen(xb, OR_BF16, i);",
+     "u += widen(w1, OR_BF16, ((int64_t)i * hidden + j) % ((int64_t)hidden * in_dim)) * widen(xb, OR_BF16, i);",
+     ["test_recall_head_matches_torch_float64"]),
 ]
 
 

@@ -389,3 +389,47 @@ def test_local_to_full_flop_ratio_at_long_context():
     cfg = orc.OracleConfig(28, 16, 8, 128, sink=4, window=2048, dtype=orc.BF16)
     a = orc.step_accounting(cfg, 131073, False)
     assert a["f_local"] * 131073 == a["f_full_always"] * 2052
+
+
+# --------------------------------------------------------------------------- recall head stand-in
+
+def _bf16_words(a) -> np.ndarray:
+    return torch.tensor(a, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_recall_head_worked_example():
+    g = _load("recall_head_worked.json")
+    q = orc.recall_head(_bf16_words(g["W1"]), np.array(g["b1"], np.float32), np.array(g["w2"], np.float32),
+                        g["b2"], _bf16_words(g["x"]))
+    assert q.tolist() == g["expect_q"]
+
+
+def test_recall_head_matches_torch_float64():
+    """Library cross-check: relu(x W1^T + b1) w2 + b2 with torch in float64 on
+    the same bf16-rounded weights and inputs."""
+    gen = torch.Generator().manual_seed(31)
+    H, I, Bn = 48, 96, 5
+    W1 = (torch.randn(H, I, generator=gen) * 0.2).to(torch.bfloat16)
+    x = torch.randn(Bn, I, generator=gen).to(torch.bfloat16)
+    b1 = torch.randn(H, generator=gen) * 0.1
+    w2 = torch.randn(H, generator=gen)
+    b2 = 0.3125  # exact in f32, the type the head's output bias is stored in
+    q = orc.recall_head(W1.view(torch.int16).numpy().view(np.uint16), b1.numpy(), w2.numpy(), b2,
+                        x.view(torch.int16).numpy().view(np.uint16))
+    ref = torch.relu(x.double() @ W1.double().T + b1.double()) @ w2.double() + b2
+    np.testing.assert_allclose(q, ref.numpy(), atol=1e-12, rtol=0)
+    assert (ref.numpy() > 0).any() and (ref.numpy() < 0).any()
+
+
+def test_recall_head_hidden_units_commute():
+    """Permuting the hidden units (rows of W1 with b1 and w2) leaves q unchanged."""
+    rng = np.random.default_rng(8)
+    H, I = 17, 40
+    W1 = _bf16_words(rng.standard_normal((H, I)) * 0.3)
+    b1 = rng.standard_normal(H).astype(np.float32)
+    w2 = rng.standard_normal(H).astype(np.float32)
+    x = _bf16_words(rng.standard_normal((3, I)))
+    perm = rng.permutation(H)
+    q0 = orc.recall_head(W1, b1, w2, -0.1, x)
+    q1 = orc.recall_head(W1[perm], b1[perm], w2[perm], -0.1, x)
+    np.testing.assert_allclose(q0, q1, atol=1e-12, rtol=0)
