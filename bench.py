@@ -55,6 +55,9 @@ def parse():
                     help="KV cache storage: bf16, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--host-kv", action="store_true",
                     help="paged history in pinned host memory (rings in HBM); the Full pass reads it over the host link")
+    ap.add_argument("--recall-head", action="store_true",
+                    help="compute the recall scores on the device with the recall-head stand-in "
+                         "(6144 -> 4608 -> 1, seeded weights, b2 set so that about rho of the steps fire)")
     ap.add_argument("--reps", type=int, default=1,
                     help="timed repetitions of the K steps from the same state (value: the median)")
     ap.add_argument("--roofline-launches", type=int, default=56)
@@ -145,8 +148,8 @@ def main() -> int:
 
     from gated_kv_access_amd import binding as B
     from gated_kv_access_amd import workloads as W
-    from gated_kv_access_amd.runner import StepRunner
-    from gated_kv_access_amd.state import DecodeState
+    from gated_kv_access_amd.runner import RecallHead, StepRunner
+    from gated_kv_access_amd.state import DecodeState, make_dims
 
     B.load()
     base, K = build_workload(args)
@@ -162,7 +165,12 @@ def main() -> int:
             log(f"paged cache of {need / 1e9:.0f} GB does not fit the {free / 1e9:.0f} GB free")
             return 1
     t0 = time.time()
-    st = DecodeState(wl, gen_device="cuda", host_cache=args.host_kv)
+    head = head_x = None
+    dims = None
+    if args.recall_head:
+        head, head_x = make_head(wl, Wm + K)
+        dims = make_dims(wl, recall_flops=head.flops)
+    st = DecodeState(wl, gen_device="cuda", host_cache=args.host_kv, dims=dims)
     st.prefill()
     q = W.gen_queries(wl, "cuda")
     k_new, v_new = st.decode_inputs()
@@ -171,7 +179,7 @@ def main() -> int:
     scores = torch.from_numpy(sc).cuda()
     log(f"setup {time.time() - t0:.1f}s")
 
-    r = StepRunner(st, q, k_new, v_new, scores, want_lse=False)
+    r = StepRunner(st, q, k_new, v_new, None if head else scores, want_lse=False, head=head, head_x=head_x)
     r.capture()
     r.replay(Wm)
     torch.cuda.synchronize()
@@ -222,6 +230,8 @@ def main() -> int:
         roofline["frac"] = round(roofline["achieved"] / host_gbps, 4)
 
     extra = {}
+    if head is not None:
+        extra["recall_head"] = recall_head_leg(head, head_x, wl.batch)
     if args.sweep:
         extra = sweep(st, wl, q, k_new, v_new, K, Wm, start_len)
 
@@ -252,6 +262,7 @@ def main() -> int:
                    "rho": list(wl.rho) if len(wl.rho) > 1 else wl.rho[0], "kv_dtype": wl.dtype,
                    "sliding_layers": len(wl.sliding_layers), "focus": bool(wl.focus),
                    "paged_history": "pinned host memory" if args.host_kv else "HBM",
+                   "recall_score": "device recall head" if head is not None else "staged input",
                    "full_calls_timed": int(f["full_calls"]), "parallelism": "single GPU"},
         "tokens_per_s": round(steps_per_s * wl.batch, 2),
         "effective_kv_gbps": round(kv_gbps, 1),
@@ -267,6 +278,48 @@ def main() -> int:
     res.update(extra)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def make_head(wl, steps):
+    """The recall-head stand-in with seeded weights and per-step inputs; b2 is the
+    (1 - rho) quantile of the scores without it, computed with torch in float32
+    (a calibration of the synthetic input, not part of the timed path)."""
+    import torch
+
+    from gated_kv_access_amd import workloads as W
+    from gated_kv_access_amd.runner import RecallHead
+
+    w1, b1, w2 = W.gen_recall_head(device="cuda")
+    hx = W.gen_head_inputs(wl, device="cuda", steps=steps).contiguous()
+    q0 = torch.relu(hx.float().reshape(-1, hx.shape[-1]) @ w1.float().T + b1) @ w2
+    rho = float(sum(wl.rho) / len(wl.rho))
+    b2 = -float(torch.quantile(q0, 1.0 - rho)) if 0.0 < rho < 1.0 else (-1e30 if rho <= 0 else 1e30)
+    head = RecallHead(w1, b1, w2, b2, wl.batch)
+    log(f"recall head: {head.params} parameters, b2 = {b2:.4f} for rho {rho}")
+    return head, hx
+
+
+def recall_head_leg(head, hx, batch, launches=50):
+    """The recall-head kernel on its own: launch time and weight-streaming rate."""
+    import torch
+
+    from gated_kv_access_amd import binding as B
+
+    s = torch.zeros(batch + 4, dtype=torch.float32, device="cuda")
+    x = hx[0].contiguous()
+    B.recall_scores(head.desc, batch, x, s, head.workspace)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(launches):
+        B.recall_scores(head.desc, batch, x, s, head.workspace)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    wbytes = head.w1.numel() * 2 + (head.b1.numel() + head.w2.numel()) * 4
+    log(f"recall head kernel: {us:.1f} us/launch, {wbytes / (us * 1e-6) / 1e9:.0f} GB/s of weights")
+    return {"params": head.params, "flops_per_request": head.flops, "us_per_launch": round(us, 2),
+            "weight_bytes": wbytes, "weight_gbps": round(wbytes / (us * 1e-6) / 1e9, 1), "launches": launches}
 
 
 def roofline_leg(args, st, wl, q, k_new, v_new):

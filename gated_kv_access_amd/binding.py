@@ -27,6 +27,7 @@ DEVERR_CAPACITY, DEVERR_BLOCK_ID, DEVERR_OUT_CAPACITY = 1, 2, 4
 EXPORTS = ("oda_workspace_size", "oda_workspace_init", "oda_prefill_kv", "oda_ring_init",
            "oda_commit_kv", "oda_decode_local", "oda_decode_full_gated", "oda_gate", "oda_step",
            "oda_access_set", "oda_stage_step", "oda_advance_counter", "oda_host_kv_pointer",
+           "oda_recall_workspace_size", "oda_recall_workspace_init", "oda_recall_scores", "oda_step_recall",
            "oda_status_string")
 
 
@@ -48,6 +49,14 @@ class OdaDims(ctypes.Structure):
         ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
         ("reserved0", ctypes.c_int32), ("recall_flops", ctypes.c_int64),
         ("layer_kind", ctypes.c_void_p),
+    ]
+
+
+class OdaRecallHead(ctypes.Structure):
+    _fields_ = [
+        ("in_dim", ctypes.c_int32), ("hidden", ctypes.c_int32),
+        ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("b2", ctypes.c_float), ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -89,6 +98,11 @@ def load(path: str = LIB_PATH):
         "oda_stage_step": (I32, [I32, P, P, P, P, I64, P]),
         "oda_advance_counter": (I32, [P, P]),
         "oda_host_kv_pointer": (I32, [P, ctypes.POINTER(ctypes.c_void_p)]),
+        "oda_recall_workspace_size": (SZ, [ctypes.POINTER(OdaRecallHead), I32]),
+        "oda_recall_workspace_init": (I32, [ctypes.POINTER(OdaRecallHead), I32, P, SZ, P]),
+        "oda_recall_scores": (I32, [ctypes.POINTER(OdaRecallHead), I32, P, P, P, SZ, P]),
+        "oda_step_recall": (I32, [D, K, I32, P, P, P, P, ctypes.POINTER(OdaRecallHead), P, P, F, P, P, P, P,
+                                  P, P, P, SZ, P, SZ, P]),
         "oda_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sig.items():
@@ -199,6 +213,40 @@ def stage_step(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor], step_
 
 def advance_counter(step_counter: torch.Tensor, stream=None) -> None:
     _check("oda_advance_counter", load().oda_advance_counter(_p(step_counter), _stream(stream)))
+
+
+def make_head(w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float) -> OdaRecallHead:
+    """Recall-head descriptor over device tensors (kept alive by the caller)."""
+    h = OdaRecallHead()
+    h.hidden, h.in_dim = int(w1.shape[0]), int(w1.shape[1])
+    h.w1, h.b1, h.w2 = _p(w1), _p(b1), _p(w2)
+    h.b2 = float(b2)
+    h.reserved0 = 0
+    return h
+
+
+def recall_workspace_size(head: OdaRecallHead, batch: int) -> int:
+    return int(load().oda_recall_workspace_size(ctypes.byref(head), batch))
+
+
+def recall_workspace_init(head: OdaRecallHead, batch: int, ws: torch.Tensor, stream=None) -> None:
+    _check("oda_recall_workspace_init", load().oda_recall_workspace_init(
+        ctypes.byref(head), batch, _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def recall_scores(head: OdaRecallHead, batch: int, x: torch.Tensor, scores: torch.Tensor, ws: torch.Tensor,
+                  stream=None) -> None:
+    _check("oda_recall_scores", load().oda_recall_scores(ctypes.byref(head), batch, _p(x), _p(scores), _p(ws),
+                                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def step_recall(dims, kv, batch, q_local, q_full, k_new, v_new, head, head_x, recall_score, theta, out, lse,
+                call_list, call_count, full_calls, counters, ws, head_ws, stream=None) -> None:
+    _check("oda_step_recall", load().oda_step_recall(
+        ctypes.byref(dims), ctypes.byref(kv), batch, _p(q_local), _p(q_full), _p(k_new), _p(v_new),
+        ctypes.byref(head), _p(head_x), _p(recall_score), float(theta), _p(out), _p(lse), _p(call_list),
+        _p(call_count), _p(full_calls), _p(counters), _p(ws), ws.numel() * ws.element_size(), _p(head_ws),
+        head_ws.numel() * head_ws.element_size(), _stream(stream)))
 
 
 def host_kv_pointer(t: torch.Tensor) -> int:

@@ -261,6 +261,73 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   return hip_status(oda::launch_attention(p, a, batch, s));
 }
 
+oda_status check_head(const oda_recall_head* h) {
+  if (!h || !h->w1 || !h->b1 || !h->w2 || h->reserved0 != 0) return ODA_ERR_INVALID_ARG;
+  if (h->in_dim < 8 || h->in_dim > 32768 || h->in_dim % 8 != 0) return ODA_ERR_INVALID_ARG;
+  if (h->hidden < 1 || h->hidden > (1 << 24) || !aligned16(h->w1) || isnan(h->b2)) return ODA_ERR_INVALID_ARG;
+  return ODA_OK;
+}
+
+oda_status check_head_ws(const oda_recall_head* h, int32_t batch, void* ws, size_t ws_bytes) {
+  oda_status st = check_head(h);
+  if (st != ODA_OK) return st;
+  if (batch < 0 || batch > ODA_MAX_BATCH) return ODA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < oda::recall_workspace_bytes(h->hidden, batch > 0 ? batch : 1)) return ODA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return ODA_ERR_WORKSPACE;
+  return ODA_OK;
+}
+
+// One decode step: Local pass of every layer; the recall head when one is
+// given (writing recall_score); the gate; the Full pass of every layer for the
+// fired requests; the fused commit.
+oda_status run_step(const Ctx& c, const oda_kv* kv, int32_t batch, const void* q_local, const void* q_full,
+                    const void* k_new, const void* v_new, const oda_recall_head* head, const void* head_x,
+                    void* head_ws, float* recall_score, float theta, float* out, float* lse,
+                    int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                    oda_stream stream) {
+  if (!q_local || !k_new || !v_new || !recall_score || !out || isnan(theta)) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q_local) || (q_full && !aligned16(q_full)) || !aligned16(k_new) || !aligned16(v_new))
+    return ODA_ERR_INVALID_ARG;
+  oda_status st = check_kv(c.plan, kv, true, true);
+  if (st != ODA_OK) return st;
+  if (batch == 0) return ODA_OK;
+  const Plan& p = c.plan;
+  const int64_t q_layer = (int64_t)batch * p.Hq * p.D * p.q_esize;
+  const int64_t kv_layer = (int64_t)batch * p.Hkv * p.D * p.esize;
+  const int64_t o_layer = (int64_t)batch * p.Hq * p.D;
+  const int64_t l_layer = (int64_t)batch * p.Hq;
+  const void* qf = q_full ? q_full : q_local;
+  auto at = [](const void* base, int64_t off) { return static_cast<const char*>(base) + off; };
+  // 1) Local pass, every layer.
+  for (int32_t l = 0; l < p.L; ++l) {
+    st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
+                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
+                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream, l + 1 < p.L ? l + 1 : -1);
+    if (st != ODA_OK) return st;
+  }
+  // 2) Recall score from the decoding state, on the device.
+  if (head) {
+    if (oda::launch_recall(*head, batch, head_x, recall_score, head_ws, stream)) return ODA_ERR_HIP;
+  }
+  // 3) Gate: compaction of the fired requests, counters.
+  int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
+  int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
+  int32_t* lens = reinterpret_cast<int32_t*>(c.base + c.ws.len_off);
+  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, lens, full_calls, counters,
+                            stream);
+  if (rc) return ODA_ERR_HIP;
+  // 4) Full recomputation of every layer for the fired requests.
+  for (int32_t l = 0; l < p.L; ++l) {
+    st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
+                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
+                  list, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
+    if (st != ODA_OK) return st;
+  }
+  // 5) Fused commit of position t for all layers.
+  return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new,
+                                       reinterpret_cast<int32_t*>(c.base + c.ws.commit_ticket_off), c.err, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -367,43 +434,47 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   Ctx c;
   oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
   if (st != ODA_OK) return st;
-  if (!q_local || !k_new || !v_new || !recall_score || !out || isnan(theta)) return ODA_ERR_INVALID_ARG;
-  if (!aligned16(q_local) || (q_full && !aligned16(q_full)) || !aligned16(k_new) || !aligned16(v_new))
-    return ODA_ERR_INVALID_ARG;
-  st = check_kv(c.plan, kv, true, true);
+  if (!recall_score) return ODA_ERR_INVALID_ARG;
+  return run_step(c, kv, batch, q_local, q_full, k_new, v_new, nullptr, nullptr, nullptr,
+                  const_cast<float*>(recall_score), theta, out, lse, call_list, call_count, full_calls, counters,
+                  stream);
+}
+
+size_t oda_recall_workspace_size(const oda_recall_head* head, int32_t batch) {
+  if (check_head(head) != ODA_OK || batch < 0 || batch > ODA_MAX_BATCH) return 0;
+  return oda::recall_workspace_bytes(head->hidden, batch > 0 ? batch : 1);
+}
+
+oda_status oda_recall_workspace_init(const oda_recall_head* head, int32_t batch, void* head_workspace,
+                                     size_t head_workspace_bytes, oda_stream stream) {
+  oda_status st = check_head_ws(head, batch, head_workspace, head_workspace_bytes);
   if (st != ODA_OK) return st;
-  if (batch == 0) return ODA_OK;
-  const Plan& p = c.plan;
-  const int64_t q_layer = (int64_t)batch * p.Hq * p.D * p.q_esize;
-  const int64_t kv_layer = (int64_t)batch * p.Hkv * p.D * p.esize;
-  const int64_t o_layer = (int64_t)batch * p.Hq * p.D;
-  const int64_t l_layer = (int64_t)batch * p.Hq;
-  const void* qf = q_full ? q_full : q_local;
-  auto at = [](const void* base, int64_t off) { return static_cast<const char*>(base) + off; };
-  // 1) Local pass, every layer.
-  for (int32_t l = 0; l < p.L; ++l) {
-    st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
-                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream, l + 1 < p.L ? l + 1 : -1);
-    if (st != ODA_OK) return st;
-  }
-  // 2) Gate: compaction of the fired requests, counters.
-  int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
-  int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
-  int32_t* lens = reinterpret_cast<int32_t*>(c.base + c.ws.len_off);
-  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, lens, full_calls, counters,
-                            stream);
-  if (rc) return ODA_ERR_HIP;
-  // 3) Full recomputation of every layer for the fired requests.
-  for (int32_t l = 0; l < p.L; ++l) {
-    st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
-                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  list, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
-    if (st != ODA_OK) return st;
-  }
-  // 4) Fused commit of position t for all layers.
-  return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new,
-                                       reinterpret_cast<int32_t*>(c.base + c.ws.commit_ticket_off), c.err, stream));
+  return hip_status(oda::launch_clear(head_workspace, oda_recall_workspace_size(head, batch), stream));
+}
+
+oda_status oda_recall_scores(const oda_recall_head* head, int32_t batch, const void* x, float* scores,
+                             void* head_workspace, size_t head_workspace_bytes, oda_stream stream) {
+  oda_status st = check_head_ws(head, batch, head_workspace, head_workspace_bytes);
+  if (st != ODA_OK) return st;
+  if (!x || !aligned16(x) || !scores) return ODA_ERR_INVALID_ARG;
+  return hip_status(oda::launch_recall(*head, batch, x, scores, head_workspace, stream));
+}
+
+oda_status oda_step_recall(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                           const void* q_local, const void* q_full, const void* k_new,
+                           const void* v_new, const oda_recall_head* head, const void* head_x,
+                           float* recall_score, float theta, float* out, float* lse,
+                           int32_t* call_list, int32_t* call_count, int64_t* full_calls,
+                           int64_t* counters, void* workspace, size_t workspace_bytes,
+                           void* head_workspace, size_t head_workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  st = check_head_ws(head, batch, head_workspace, head_workspace_bytes);
+  if (st != ODA_OK) return st;
+  if (!head_x || !aligned16(head_x) || !recall_score) return ODA_ERR_INVALID_ARG;
+  return run_step(c, kv, batch, q_local, q_full, k_new, v_new, head, head_x, head_workspace, recall_score, theta,
+                  out, lse, call_list, call_count, full_calls, counters, stream);
 }
 
 oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t b,

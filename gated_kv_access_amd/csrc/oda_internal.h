@@ -113,6 +113,12 @@ int launch_clear(void* ptr, size_t bytes, oda_stream s);
 int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
                  int64_t* counter, int64_t num_steps, oda_stream s);
 int launch_advance(int64_t* counter, oda_stream s);
+// Recall head: number of workgroups for `hidden` units, the head workspace
+// size, and the launch.
+int recall_groups(int32_t hidden);
+size_t recall_workspace_bytes(int32_t hidden, int32_t batch);
+int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float* scores, void* ws,
+                  oda_stream s);
 // Device address of pinned host memory: 0, 1 (not pinned host memory) or 2 (runtime error).
 int host_device_pointer(void* host_ptr, void** device_ptr);
 // Rows per workgroup iteration for the attention kernel built for (dtype, d).

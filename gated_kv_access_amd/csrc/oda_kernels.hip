@@ -1480,6 +1480,178 @@ int launch_advance(int64_t* counter, oda_stream s) {
   return (int)hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// recall head stand-in: q = w2 . max(W1 x + b1, 0) + b2 for every request
+
+constexpr int kRecallRowsPerWave = 2;        // hidden units per wave (one workgroup: 16)
+constexpr int kRecallBatchChunk = 8;         // requests whose x sits in LDS at once
+constexpr int kRecallLdsBytes = 48 * 1024;   // x chunk: at most this many bytes
+constexpr int kRecallVecs = 4;               // 16-byte W1 vectors per lane per row in flight
+
+struct RecallParams {
+  int32_t in_dim, hidden, batch, chunk;  // chunk: requests per LDS round (<= kRecallBatchChunk)
+  const uint4* w1;
+  const float* b1;
+  const float* w2;
+  float b2;
+  const uint4* x;
+  float* scores;
+  float* partial;   // [groups][batch]
+  int32_t* ticket;  // zero between launches
+};
+
+// Workgroup g owns hidden units [16 g, 16 g + 16), two per wave.  For each
+// chunk of requests the x rows are staged in LDS; every wave streams its two
+// W1 rows once per chunk with 16-byte loads (both rows' next four vectors per
+// lane in flight together), multiplies them with every staged x row and adds
+// w2_j max(u_j, 0) into per-request sums.  The workgroup's sums are published
+// device-wide and the last workgroup adds all of them with b2.
+__global__ __launch_bounds__(kGroupThreads) void recall_kernel(RecallParams P) {
+  extern __shared__ uint4 s_x[];  // [chunk][in_dim / 8]
+  __shared__ float s_part[kWavesPerGroup][kRecallBatchChunk];
+  __shared__ int32_t s_last;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int32_t vecs = P.in_dim / 8;  // 16-byte vectors per row
+  const int32_t row0 = blockIdx.x * (kWavesPerGroup * kRecallRowsPerWave) + wave * kRecallRowsPerWave;
+  bool live[kRecallRowsPerWave];
+  const uint4* wrow[kRecallRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRecallRowsPerWave; ++r) {
+    live[r] = row0 + r < P.hidden;
+    wrow[r] = P.w1 + (int64_t)(live[r] ? row0 + r : 0) * vecs;
+  }
+  for (int32_t c0 = 0; c0 < P.batch; c0 += P.chunk) {
+    const int32_t nb = min(P.chunk, P.batch - c0);
+    __syncthreads();  // the previous chunk's LDS reads are done
+    for (int32_t i = threadIdx.x; i < nb * vecs; i += kGroupThreads)
+      s_x[i] = P.x[(int64_t)c0 * vecs + i];
+    __syncthreads();
+    float acc[kRecallRowsPerWave][kRecallBatchChunk];
+#pragma unroll
+    for (int r = 0; r < kRecallRowsPerWave; ++r)
+#pragma unroll
+      for (int b = 0; b < kRecallBatchChunk; ++b) acc[r][b] = 0.f;
+    for (int32_t v0 = 0; v0 < vecs; v0 += kWave * kRecallVecs) {
+      uint4 w[kRecallRowsPerWave][kRecallVecs];
+#pragma unroll
+      for (int r = 0; r < kRecallRowsPerWave; ++r)
+#pragma unroll
+        for (int k = 0; k < kRecallVecs; ++k) {
+          const int32_t v = v0 + k * kWave + lane;
+          w[r][k] = (live[r] && v < vecs) ? wrow[r][v] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int k = 0; k < kRecallVecs; ++k) {
+        const int32_t v = v0 + k * kWave + lane;
+        if (v >= vecs) break;
+#pragma unroll
+        for (int b = 0; b < kRecallBatchChunk; ++b) {
+          if (b < nb) {
+            const uint4 xv = s_x[b * vecs + v];
+#pragma unroll
+            for (int r = 0; r < kRecallRowsPerWave; ++r) {
+              float a = acc[r][b];
+              a = dot2_bf16(w[r][k].x, xv.x, a);
+              a = dot2_bf16(w[r][k].y, xv.y, a);
+              a = dot2_bf16(w[r][k].z, xv.z, a);
+              a = dot2_bf16(w[r][k].w, xv.w, a);
+              acc[r][b] = a;
+            }
+          }
+        }
+      }
+    }
+    float sums[kRecallBatchChunk];
+#pragma unroll
+    for (int b = 0; b < kRecallBatchChunk; ++b) sums[b] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRecallRowsPerWave; ++r) {
+      if (!live[r]) continue;  // uniform across the wave
+      const float b1 = P.b1[row0 + r], w2 = P.w2[row0 + r];
+#pragma unroll
+      for (int b = 0; b < kRecallBatchChunk; ++b) {
+        if (b < nb) {
+          const float u = sum_over<1, 32>(acc[r][b]) + b1;
+          sums[b] = fmaf(w2, fmaxf(u, 0.f), sums[b]);
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < kRecallBatchChunk; ++b) s_part[wave][b] = sums[b];
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerGroup; ++w) t += s_part[w][threadIdx.x];
+      publish(P.partial + (int64_t)blockIdx.x * P.batch + c0 + threadIdx.x, t);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t prev = __hip_atomic_fetch_add(P.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (int32_t)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // One wave per request: every lane loads up to eight partials at once, then
+  // the wave adds them.
+  const int32_t groups = (int32_t)gridDim.x;
+  for (int32_t b = wave; b < P.batch; b += kWavesPerGroup) {
+    float t = 0.f;
+    for (int32_t g0 = 0; g0 < groups; g0 += 8 * kWave) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int32_t g = g0 + k * kWave + lane;
+        v[k] = g < groups ? collect(P.partial + (int64_t)g * P.batch + b) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t += v[k];
+    }
+    t = sum_over<1, 32>(t);
+    if (lane == 0) P.scores[b] = t + P.b2;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(P.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int recall_groups(int32_t hidden) {
+  const int32_t per = kWavesPerGroup * kRecallRowsPerWave;
+  return (hidden + per - 1) / per;
+}
+
+size_t recall_workspace_bytes(int32_t hidden, int32_t batch) {
+  // ticket word, then the partial sums
+  return 256 + ((sizeof(float) * (size_t)recall_groups(hidden) * (size_t)batch + 255) & ~(size_t)255);
+}
+
+int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float* scores, void* ws,
+                  oda_stream s) {
+  if (batch <= 0) return 0;
+  RecallParams P{};
+  P.in_dim = h.in_dim;
+  P.hidden = h.hidden;
+  P.batch = batch;
+  const int32_t row_bytes = h.in_dim * 2;
+  int32_t chunk = kRecallLdsBytes / row_bytes;
+  if (chunk > kRecallBatchChunk) chunk = kRecallBatchChunk;
+  if (chunk < 1) chunk = 1;
+  P.chunk = chunk;
+  P.w1 = static_cast<const uint4*>(h.w1);
+  P.b1 = h.b1;
+  P.w2 = h.w2;
+  P.b2 = h.b2;
+  P.x = static_cast<const uint4*>(x);
+  P.scores = scores;
+  P.ticket = static_cast<int32_t*>(ws);
+  P.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  const size_t lds = (size_t)chunk * row_bytes;
+  hipLaunchKernelGGL(recall_kernel, dim3(recall_groups(h.hidden)), dim3(kGroupThreads), lds, s, P);
+  return (int)hipGetLastError();
+}
+
 int host_device_pointer(void* host_ptr, void** device_ptr) {
   hipPointerAttribute_t attr{};
   if (hipPointerGetAttributes(&attr, host_ptr) != hipSuccess) {

@@ -227,3 +227,27 @@ def gen_block_table(wl: Workload, spare_blocks: int = 0) -> Tuple[np.ndarray, in
         table[b, :need[b]] = perm[off:off + need[b]]
         off += need[b]
     return table, total
+
+
+# Recall-head stand-in: the pages give R_psi's inputs (h_{t-1}, E(x_t), h^L_t
+# of a 2048-wide model) and its size on Qwen3-1.7B (28,325,889 parameters),
+# not its layers.  One hidden ReLU layer 6144 -> 4608 -> 1 holds 28,320,769.
+HEAD_IN_DIM, HEAD_HIDDEN = 3 * 2048, 4608
+
+
+def gen_recall_head(in_dim: int = HEAD_IN_DIM, hidden: int = HEAD_HIDDEN, seed: int = 7, device="cpu"):
+    """Seeded stand-in weights (no trained values exist here): W1 bf16 with
+    N(0, 1/in_dim) entries, b1 ~ N(0, 0.1^2), w2 ~ N(0, 2/hidden), all f32 but W1."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(seed, 29, in_dim, hidden))
+    w1 = (torch.randn((hidden, in_dim), generator=g, device=device) * in_dim ** -0.5).to(torch.bfloat16)
+    b1 = torch.randn(hidden, generator=g, device=device) * 0.1
+    w2 = torch.randn(hidden, generator=g, device=device) * (2.0 / hidden) ** 0.5
+    return w1.contiguous(), b1.contiguous(), w2.contiguous()
+
+
+def gen_head_inputs(wl: Workload, in_dim: int = HEAD_IN_DIM, device="cpu", steps: Optional[int] = None) -> torch.Tensor:
+    """Per-step decoding-state inputs [steps][B][in_dim] of the recall head:
+    [h_{t-1}; E(x_t); h^L_t] drawn N(0,1) and rounded to bf16."""
+    n = wl.steps if steps is None else steps
+    return _normal((n, wl.batch, in_dim), _seed(wl.seed, 31, in_dim), device, torch.bfloat16)

@@ -246,6 +246,52 @@ oda_status oda_advance_counter(int64_t* step_counter, oda_stream stream);
  * not pinned host memory, ODA_ERR_HIP if the runtime call fails. */
 oda_status oda_host_kv_pointer(void* host_ptr, void** device_ptr);
 
+/* Recall-head stand-in.  The recall score is q_t = R_psi(h_{t-1}, E(x_t), h^L_t)
+ * (picx.dev summary, "Local-First Decoding"): a small trained module reading
+ * the previous hidden state, the current token's embedding and the hidden
+ * state the Local pass produced; on Qwen3-1.7B it holds 28,325,889 parameters
+ * (learnaivisually explainer, glossary).  The pages do not give its layers;
+ * this stand-in is one hidden ReLU layer:
+ *     x = [h_{t-1}; E(x_t); h^L_t]   (in_dim values, bf16)
+ *     q = w2 . max(W1 x + b1, 0) + b2
+ * All pointers are device pointers; the caller owns them. */
+typedef struct {
+  int32_t in_dim;              /* length of x, a multiple of 8, <= 32768          */
+  int32_t hidden;              /* hidden units, >= 1                              */
+  const void* w1;              /* bf16 [hidden][in_dim], 16-byte aligned           */
+  const float* b1;             /* [hidden]                                        */
+  const float* w2;             /* [hidden]                                        */
+  float b2;
+  int32_t reserved0;           /* must be 0                                       */
+} oda_recall_head;
+
+/* Host.  Bytes of the recall head's own workspace for `batch` requests (its
+ * per-workgroup partial sums and a ticket word); 0 on invalid arguments. */
+size_t oda_recall_workspace_size(const oda_recall_head* head, int32_t batch);
+
+/* Recall scores of `batch` requests: x bf16 [batch][in_dim] (16-byte aligned)
+ * -> scores [batch] f32.  One kernel; its last workgroup adds the partial sums.
+ * The workspace must be zeroed once after allocation (oda_recall_workspace_init). */
+oda_status oda_recall_scores(const oda_recall_head* head, int32_t batch, const void* x, float* scores,
+                             void* head_workspace, size_t head_workspace_bytes, oda_stream stream);
+
+/* Zeroes the recall head's workspace (a small kernel). */
+oda_status oda_recall_workspace_init(const oda_recall_head* head, int32_t batch, void* head_workspace,
+                                     size_t head_workspace_bytes, oda_stream stream);
+
+/* oda_step with the recall score computed on the device between the Local
+ * passes and the gate, as "Local-First Decoding" orders them: Local pass of
+ * every layer, recall head over head_x [batch][in_dim] (writing recall_score
+ * [batch], which the gate then reads), gate, Full pass of every layer for the
+ * fired requests, fused commit.  Other arguments as for oda_step. */
+oda_status oda_step_recall(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                           const void* q_local, const void* q_full, const void* k_new,
+                           const void* v_new, const oda_recall_head* head, const void* head_x,
+                           float* recall_score, float theta, float* out, float* lse,
+                           int32_t* call_list, int32_t* call_count, int64_t* full_calls,
+                           int64_t* counters, void* workspace, size_t workspace_bytes,
+                           void* head_workspace, size_t head_workspace_bytes, oda_stream stream);
+
 /* Host.  Human-readable status name. */
 const char* oda_status_string(oda_status status);
 
