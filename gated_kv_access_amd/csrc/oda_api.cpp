@@ -199,7 +199,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
                     const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
                     const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
                     const float* score, float theta, int32_t* list_out, int32_t* count_out,
-                    oda_stream s, int32_t warm_layer = -1) {
+                    oda_stream s) {
   const Plan& p = c.plan;
   const bool gated = p.kind[layer] == ODA_LAYER_GATED;
   const bool full = gate != oda::kGateAll;
@@ -250,14 +250,6 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
-  if (warm_layer >= 0 && a.rows.source == oda::kSrcRing) {
-    const bool wg = p.kind[warm_layer] == ODA_LAYER_GATED;
-    const int32_t slots = wg ? p.ring_slots : p.sw_window;
-    const int64_t layer_bytes = (int64_t)p.max_batch * p.Hkv * slots * row_bytes;
-    a.pf_k = static_cast<const char*>(wg ? kv->k_ring : kv->k_swring) + p.kidx[warm_layer] * layer_bytes;
-    a.pf_v = static_cast<const char*>(wg ? kv->v_ring : kv->v_swring) + p.kidx[warm_layer] * layer_bytes;
-    a.pf_slots = slots;
-  }
   return hip_status(oda::launch_attention(p, a, batch, s));
 }
 
@@ -302,7 +294,7 @@ oda_status run_step(const Ctx& c, const oda_kv* kv, int32_t batch, const void* q
   for (int32_t l = 0; l < p.L; ++l) {
     st = run_pass(c, kv, l, batch, oda::kGateAll, at(q_local, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream, l + 1 < p.L ? l + 1 : -1);
+                  nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 2) Recall score from the decoding state, on the device.

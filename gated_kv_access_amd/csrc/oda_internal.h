@@ -86,13 +86,6 @@ struct AttnParams {
   uint32_t* err;
   float scale_log2;           // softmax scale * k_scale * log2(e)
   float v_scale;              // applied to the merged output
-  // Ring passes of a step: the next layer's ring ([max_batch][Hkv][pf_slots][d]),
-  // whose rows of this workgroup's tiles are read into L2 once this
-  // workgroup's partial is out (the next layer's workgroup of the same index
-  // runs on the same XCD).  NULL: no warming.
-  const void* pf_k;
-  const void* pf_v;
-  int32_t pf_slots;
 };
 
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.

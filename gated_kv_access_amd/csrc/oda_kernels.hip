@@ -810,31 +810,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     s_last = prev == used - 1;
   }
   __syncthreads();
-  if (!s_last) {
-    if constexpr (SRC == kSrcRing) {
-      if (P.pf_k != nullptr) {
-        // Warm L2 with the next layer's ring rows of this workgroup's tiles.
-        const char* pk = static_cast<const char*>(P.pf_k) + ((int64_t)b * P.Hkv + g) * P.pf_slots * D * ES;
-        const char* pv = static_cast<const char*>(P.pf_v) + ((int64_t)b * P.Hkv + g) * P.pf_slots * D * ES;
-        uint32_t sink = 0;
-        for (int32_t tile = tile_begin; tile < tile_end; ++tile) {
-#pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
-            if (row < P.pf_slots) {
-#pragma unroll
-              for (int j = 0; j < NV; ++j) {
-                const int64_t off = (int64_t)row * D * ES + (j * LPR + sub) * 16;
-                sink ^= reinterpret_cast<const uint4*>(pk + off)->x ^ reinterpret_cast<const uint4*>(pv + off)->x;
-              }
-            }
-          }
-        }
-        asm volatile("" ::"v"(sink));
-      }
-    }
-    return;
-  }
+  if (!s_last) return;
   merge_and_write<DT, D, G>(P, b, g, used);
   if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[(int64_t)b * P.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
