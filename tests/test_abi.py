@@ -180,3 +180,12 @@ def test_workspace_size_is_deterministic_and_monotone_in_batch(lib):
     sizes = [lib.oda_workspace_size(ctypes.byref(d), b) for b in (1, 2, 8, 64)]
     assert all(s > 0 for s in sizes)
     assert sizes == [lib.oda_workspace_size(ctypes.byref(d), b) for b in (1, 2, 8, 64)]
+
+
+def test_empty_batch_is_a_no_op(lib):
+    """batch 0: every call validates and returns ODA_OK without launching (no GPU here)."""
+    d, kv = _dims(), _kv()
+    ws = _ws(lib, d, 0)
+    assert ws > 0
+    assert lib.oda_step(ctypes.byref(d), ctypes.byref(kv), 0, FAKE, None, FAKE, FAKE, FAKE, 0.0, FAKE, None,
+                        None, None, None, None, FAKE, ws, None) == 0

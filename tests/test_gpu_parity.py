@@ -102,6 +102,24 @@ def test_local_equals_full_while_t_within_s_plus_w():
     assert r_full.full_calls.tolist() == [wl.steps] * wl.batch
 
 
+EDGE = [
+    _small("block_size_1", block_size=1, prefill=(0, 40, 301), steps=6, seed=161),
+    _small("block_size_2_fp8", block_size=2, prefill=(3, 90, 513), steps=6, seed=162).fp8(),
+    _small("window_1", sink=4, window=1, prefill=(0, 3, 700), steps=8, seed=163),
+    _small("sinks_over_window", sink=40, window=8, prefill=(0, 30, 60), steps=20, seed=164),
+    _small("ring_exactly_one_tile", sink=4, window=124, prefill=(120, 127, 128), steps=6, seed=165),
+    _small("one_request_f32_d64", dtype="f32", head_dim=64, num_q_heads=1, num_kv_heads=1, batch=1,
+           prefill=(2049,), steps=4, seed=166),
+]
+
+
+@pytest.mark.parametrize("wl", EDGE, ids=[w.name for w in EDGE])
+def test_edge_shapes_match_oracle(wl):
+    """Every row its own block, a one-slot window, more sinks than window
+    slots, a ring of exactly one tile (plus the current token), GQA group 1."""
+    _check_run(wl)
+
+
 HYBRID = [
     _small("hybrid_full", num_layers=8, sw_window=64, sink=4, window=128, batch=2, prefill=(1000, 2500),
            steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)), seed=121),
