@@ -20,7 +20,7 @@ namespace {
 
 constexpr int32_t kComputeUnits = 256;        // MI355X: one 8-wave workgroup fills a CU
 constexpr int32_t kFullRowsPerSplit = 16384;  // beyond this, more rounds of workgroups
-constexpr int32_t kMaxSplits = 512;           // merge weights are staged in LDS
+constexpr int32_t kMaxSplits = 512;           // bounds the workspace's partials per (request, head)
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 

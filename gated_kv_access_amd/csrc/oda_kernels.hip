@@ -10,12 +10,14 @@
 // of eight wave64s owns one (split, KV head, request) and streams its rows of
 // K and V with 16-byte loads: every lane holds four 16-byte chunks of a row, so
 // a 256-byte row (bf16, d = 128) is spread over 4 lanes and one wave covers 16
-// rows per pass (FP8 E4M3 rows: two chunks per lane, two passes per tile).  All query heads of a GQA group use each loaded row.  Scores
-// are reduced across the lanes of a row with DPP, the running maximum is kept
-// per wave (log2 domain, fp32), and each workgroup leaves one (o, m, l) partial
-// per query head.  The last workgroup of each (request, KV head) to finish --
-// found with a ticket counter in the workspace -- folds the partials and the
-// current token (position t, which the caches do not hold yet) into the output.
+// rows per pass (FP8 E4M3 rows: two chunks per lane, two passes per tile).
+// All query heads of a GQA group use each loaded row.  Scores are reduced
+// across the lanes of a row with DPP and kept in the log2 domain against a
+// per-lane reference maximum; the current token (position t, which the caches
+// do not hold yet) is one more row, read from k_cur / v_cur by the last split.
+// Each workgroup leaves one (o, m, l) partial per query head, and the last
+// workgroup of each (request, KV head) to finish -- found with a ticket counter
+// in the workspace -- merges the partials into the output.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -350,7 +352,7 @@ __device__ void write_call_list(const AttnParams& P) {
 }
 
 // ----------------------------------------------------------------------------
-// merge of the split partials and the current token (run by one workgroup)
+// merge of the split partials (run by one workgroup)
 
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
