@@ -376,10 +376,11 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
   float M = -INFINITY, L = 0.f, acc = 0.f;
   for (int32_t base = 0; base < used; base += kMergeBatch) {
     const int32_t n = used - base < kMergeBatch ? used - base : kMergeBatch;
+    // Branch-free: slots past the round's end re-read its last partial (their
+    // weights are zero below), so all loads leave back to back.
     float x[kMergeBatch];
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
-      if (i < n) x[i] = collect(po + (int64_t)(base + i) * D);
+    for (int i = 0; i < kMergeBatch; ++i) x[i] = collect(po + (int64_t)(base + (i < n ? i : n - 1)) * D);
     float mi = -INFINITY, li = 0.f;
     if (lane < n) {
       const uint64_t w2 = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(ml + 2 * (base + lane))),
@@ -393,8 +394,8 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
     L = fmaf(L, keep, sum_over<1, 32>(wi * li));
     acc *= keep;
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
-      if (i < n) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], acc);
+    for (int i = 0; i < kMergeBatch; ++i)  // lanes >= n hold weight 0
+      acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], acc);
     M = m_new;
   }
   P.out[(head0 + h) * D + e] = acc / L * P.v_scale;
