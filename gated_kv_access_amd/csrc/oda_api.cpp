@@ -82,7 +82,8 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
   const float k_scale = d->k_scale > 0.f ? d->k_scale : 1.f;
   p->scale_log2 = scale * k_scale * 1.44269504088896340736f;
   p->v_scale = d->v_scale > 0.f ? d->v_scale : 1.f;
-  p->tile_rows = oda::tile_rows_for(p->dtype, p->D);
+  p->tile_rows = oda::tile_rows_for(p->dtype, p->D, oda::kSrcPaged);
+  p->ring_tile_rows = oda::tile_rows_for(p->dtype, p->D, oda::kSrcRing);
   return ODA_OK;
 }
 
@@ -110,7 +111,7 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     // leave the chip unfilled; at larger batches a single round of workgroups,
     // each taking several tiles, so that no workgroup's fixed cost is paid twice
     // per CU.
-    const int32_t rtiles = ceil_div(p->ring_slots + 1, tile);
+    const int32_t rtiles = ceil_div(p->ring_slots + 1, p->ring_tile_rows);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
     int32_t l = d->local_splits > 0 ? d->local_splits : round;
@@ -119,7 +120,7 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
-    const int32_t stiles = ceil_div(p->sw_window + 1, tile);
+    const int32_t stiles = ceil_div(p->sw_window + 1, p->ring_tile_rows);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
     int32_t s = d->local_splits > 0 ? d->local_splits : round;

@@ -28,7 +28,8 @@ struct Plan {
   uint8_t kind[ODA_MAX_LAYERS];
   int16_t kidx[ODA_MAX_LAYERS];  // rank of the layer among layers of its kind
   int32_t full_splits, local_splits, sw_splits;
-  int32_t tile_rows;  // rows one workgroup consumes per iteration
+  int32_t tile_rows;       // rows one workgroup consumes per iteration: paged passes
+  int32_t ring_tile_rows;  // the same for ring passes
   float scale_log2;   // softmax scale * k_scale * log2(e)
   float v_scale;
   int64_t recall_flops;
@@ -114,7 +115,7 @@ int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float*
                   oda_stream s);
 // Device address of pinned host memory: 0, 1 (not pinned host memory) or 2 (runtime error).
 int host_device_pointer(void* host_ptr, void** device_ptr);
-// Rows per workgroup iteration for the attention kernel built for (dtype, d).
-int tile_rows_for(int32_t dtype, int32_t head_dim);
+// Rows per workgroup iteration for the attention kernel built for (dtype, d, source).
+int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source);
 
 }  // namespace oda

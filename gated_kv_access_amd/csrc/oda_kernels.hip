@@ -77,6 +77,20 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, true));
 }
 
+// Sum over the LPR consecutive lanes that hold one K/V row (LPR = 2..16,
+// aligned groups), left in every lane of the group: quad permutations, then
+// the half-row and row mirrors (DPP, no LDS).
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += xor_lane<1>(v);
+  if constexpr (LPR >= 4) v += xor_lane<2>(v);
+  if constexpr (LPR >= 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (LPR >= 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));  // row_mirror
+  return v;
+}
+
 // Sum / max over the lanes of a 16-lane row that are congruent modulo STEP
 // (the row groups when a K/V row spans STEP lanes).
 template <int STEP>
@@ -139,25 +153,30 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 }
 
 // Register geometry of one K/V row.  A row is spread over LPR lanes; each lane
-// holds NV 16-byte vectors of it (bf16 / f32: four, FP8: two, so an FP8 lane
-// keeps the same 32 elements per row as a bf16 lane and the freed tile
-// registers carry a second pass of rows instead).
-template <int DT, int D>
+// holds NV 16-byte vectors of it.  Paged passes stream: four vectors per lane
+// (bf16, f32) or two (FP8, whose freed tile registers carry a second pass of
+// rows), so a lane's loads are large and its accumulators serve a long run of
+// rows.  Ring passes take one 128-row tile per workgroup and are bound by
+// latency: there a lane holds a single vector of each row (a bf16 d-128 row
+// spans a whole 16-lane DPP row) over several passes, which keeps the lane's
+// accumulators, and so the fold at the end of the pass, small.
+template <int DT, int D, int SRC = kSrcPaged>
 struct Geo {
   static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
   static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
-  static constexpr int NV = DT == ODA_FP8_E4M3 ? 2 : 4;  // 16-byte K/V vectors per lane per row
   static constexpr int ROW_BYTES = D * ES;
+  static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16;
+  static constexpr int NV = WIDE ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 4);  // 16-byte K/V vectors per lane per row
   static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
   static constexpr int RPP = kWave / LPR;            // rows per wave pass
   static constexpr int EPV = 16 / ES;                // elements per 16-byte K/V vector
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = DT == ODA_FP8_E4M3 ? 2 : 1;  // passes per wave per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1);  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
-  static_assert(LPR >= 2 && LPR <= 8, "row must span 2..8 lanes");
-  static_assert(QV % NV == 0, "whole query vectors per K/V vector");
+  static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
+  static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
 };
 
 // One element of a stored K/V row and of a query row, widened to f32.
@@ -407,7 +426,7 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
 
 template <int DT, int D, int G, int SRC, bool BALLOT>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
-  using Gm = Geo<DT, D>;
+  using Gm = Geo<DT, D, SRC>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
   constexpr int TILE = Gm::TILE;
@@ -628,7 +647,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
             acc = fmaf(__uint_as_float(kk.w), __uint_as_float(qq.w), acc);
           }
         }
-        acc = sum_over<1, LPR / 2>(acc);
+        acc = lane_group_sum<LPR>(acc);
         s[i][h] = R.valid[i] ? acc * P.scale_log2 : -INFINITY;
       }
     }
@@ -1234,10 +1253,16 @@ int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_st
 
 }  // namespace
 
-int tile_rows_for(int32_t dtype, int32_t head_dim) {
-  if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128>::TILE : Geo<ODA_BF16, 64>::TILE;
-  if (dtype == ODA_FP8_E4M3) return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128>::TILE : Geo<ODA_FP8_E4M3, 64>::TILE;
-  return head_dim == 128 ? Geo<ODA_F32, 128>::TILE : Geo<ODA_F32, 64>::TILE;
+template <int SRC>
+int tile_rows_src(int32_t dtype, int32_t head_dim) {
+  if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128, SRC>::TILE : Geo<ODA_BF16, 64, SRC>::TILE;
+  if (dtype == ODA_FP8_E4M3)
+    return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128, SRC>::TILE : Geo<ODA_FP8_E4M3, 64, SRC>::TILE;
+  return head_dim == 128 ? Geo<ODA_F32, 128, SRC>::TILE : Geo<ODA_F32, 64, SRC>::TILE;
+}
+
+int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source) {
+  return source == kSrcRing ? tile_rows_src<kSrcRing>(dtype, head_dim) : tile_rows_src<kSrcPaged>(dtype, head_dim);
 }
 
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {
