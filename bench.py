@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--reps", type=int, default=1,
                     help="timed repetitions of the K steps from the same state (value: the median)")
     ap.add_argument("--roofline-launches", type=int, default=56)
+    ap.add_argument("--full-splits", type=int, default=0,
+                    help="split-K ranges per (request, KV head) of Full passes (0: the library's choice)")
+    ap.add_argument("--local-splits", type=int, default=0,
+                    help="split-K ranges per (request, KV head) of ring passes (0: the library's choice)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time rho=0, rho=1 and always-Full for the savings check")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,10 +177,10 @@ def main() -> int:
             return 1
     t0 = time.time()
     head = head_x = None
-    dims = None
     if args.recall_head:
         head, head_x = make_head(wl, Wm + K)
-        dims = make_dims(wl, recall_flops=head.flops)
+    dims = make_dims(wl, full_splits=args.full_splits, local_splits=args.local_splits,
+                     recall_flops=head.flops if head else 0)
     st = DecodeState(wl, gen_device="cuda", host_cache=args.host_kv, dims=dims)
     st.prefill()
     q = W.gen_queries(wl, "cuda")

@@ -20,7 +20,8 @@ namespace {
 
 constexpr int32_t kComputeUnits = 256;        // MI355X: one 8-wave workgroup fills a CU
 constexpr int32_t kFullRowsPerSplit = 16384;  // beyond this, more rounds of workgroups
-constexpr int32_t kMaxSplits = 512;           // bounds the workspace's partials per (request, head)
+constexpr int32_t kMaxSplits = 512;
+constexpr int32_t kSplitRowUnit = 16;         // split ranges are whole units of this many rows (kernel side too)           // bounds the workspace's partials per (request, head)
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
@@ -103,8 +104,10 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
       const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)(kComputeUnits / pairs);
       f = ceil_div(max_ctx, kFullRowsPerSplit);
       f = ceil_div(f, round) * round;
+      if (f > tiles) f = tiles;
     }
-    if (f > tiles) f = tiles;
+    const int32_t units = ceil_div(max_ctx + 1, kSplitRowUnit);
+    if (f > units) f = units;
     if (f > kMaxSplits) f = kMaxSplits;
     p->full_splits = f < 1 ? 1 : f;
     // Ring passes: one tile per workgroup while the (request, KV head) pairs
@@ -112,19 +115,21 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     // each taking several tiles, so that no workgroup's fixed cost is paid twice
     // per CU.
     const int32_t rtiles = ceil_div(p->ring_slots + 1, p->ring_tile_rows);
+    const int32_t runits = ceil_div(p->ring_slots + 1, kSplitRowUnit);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
-    int32_t l = d->local_splits > 0 ? d->local_splits : round;
-    if (l > rtiles) l = rtiles;
+    int32_t l = d->local_splits > 0 ? d->local_splits : (round < rtiles ? round : rtiles);
+    if (l > runits) l = runits;
     if (l > kMaxSplits) l = kMaxSplits;
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
     const int32_t stiles = ceil_div(p->sw_window + 1, p->ring_tile_rows);
+    const int32_t sunits = ceil_div(p->sw_window + 1, kSplitRowUnit);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
-    int32_t s = d->local_splits > 0 ? d->local_splits : round;
-    if (s > stiles) s = stiles;
+    int32_t s = d->local_splits > 0 ? d->local_splits : (round < stiles ? round : stiles);
+    if (s > sunits) s = sunits;
     if (s > kMaxSplits) s = kMaxSplits;
     p->sw_splits = s < 1 ? 1 : s;
   }

@@ -317,12 +317,19 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
 }
 
 // Splitting n_rows over `splits` workgroups in whole tiles.
-__device__ __forceinline__ void split_tiles(int32_t n_rows, int32_t tile, int32_t splits, int32_t& per,
-                                            int32_t& used) {
-  const int32_t n_tiles = (n_rows + tile - 1) / tile;
-  per = (n_tiles + splits - 1) / splits;
-  if (per < 1) per = 1;
-  used = (n_tiles + per - 1) / per;
+// Rows [0, n) of a pass go to `splits` contiguous ranges made of whole units of
+// kSplitRowUnit rows, as even as whole units allow (range sizes differ by one
+// unit at most, so no workgroup of a launch carries a whole tile more than
+// another).  The first `used` ranges are non-empty; `split` < `used` gets
+// [begin, end).
+constexpr int32_t kSplitRowUnit = 16;
+__device__ __forceinline__ void split_rows(int32_t n, int32_t splits, int32_t split, int32_t& used,
+                                           int32_t& begin, int32_t& end) {
+  const int32_t units = (n + kSplitRowUnit - 1) / kSplitRowUnit;
+  used = units < splits ? units : splits;
+  if (used < 1) used = 1;
+  begin = (int32_t)((int64_t)split * units / used) * kSplitRowUnit;
+  end = split + 1 >= used ? n : (int32_t)((int64_t)(split + 1) * units / used) * kSplitRowUnit;
 }
 
 // ----------------------------------------------------------------------------
@@ -477,11 +484,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
   // Row n_rows is the current token t, read from k_cur / v_cur: it is
   // processed like any other row, by the last split.
-  int32_t per, used;
-  split_tiles(n_rows + 1, TILE, P.splits, per, used);
+  int32_t used, row_begin, row_end;
+  split_rows(n_rows + 1, P.splits, split, used, row_begin, row_end);
   if (split >= used) return;
-  const int32_t tile_begin = split * per;
-  const int32_t tile_end = min(tile_begin + per, (n_rows + TILE) / TILE);
+  // Tiles of this split: rows row_begin + k * TILE ...; rows at or past row_end
+  // belong to the next split and stay out of the sums.
+  const int32_t n_tiles = (row_end - row_begin + TILE - 1) / TILE;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -538,8 +546,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     for (int i = 0; i < NP; ++i) {
       B.blk[i] = -1;
       if constexpr (SRC == kSrcPaged) {
-        const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
-        if (tile < tile_end && row < n_rows) {
+        const int32_t row = row_begin + tile * TILE + (wave * NP + i) * RPP + rrow;
+        if (tile < n_tiles && row < row_end && row < n_rows) {
           const int32_t p = interval_position(iv, row);
           B.blk[i] = btab[(p - 1) >> P.block_shift];
         }
@@ -549,9 +557,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int32_t row = tile * TILE + (wave * NP + i) * RPP + rrow;
+      const int32_t row = row_begin + tile * TILE + (wave * NP + i) * RPP + rrow;
       R.row[i] = row;
-      bool ok = row <= n_rows;
+      bool ok = row < row_end;  // row_end <= n_rows + 1
       const char* kb = kbase;
       const char* vb = vbase;
       int64_t off = 0;
@@ -713,22 +721,22 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 
   TileRegs ra, rb;
   BlockIds ba, bb;
-  resolve_blocks(tile_begin, ba);
-  resolve_blocks(tile_begin + 1, bb);
-  load_tile(tile_begin, ba, ra);
+  resolve_blocks(0, ba);
+  resolve_blocks(1, bb);
+  load_tile(0, ba, ra);
   if constexpr (SRC == kSrcRing) {
     if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
     t = committed + 1;
     rst = ring_state(t, P.rows.sink, P.rows.window);
   }
-  for (int32_t tile = tile_begin; tile < tile_end; tile += 2) {
-    const bool has_b = tile + 1 < tile_end;
+  for (int32_t tile = 0; tile < n_tiles; tile += 2) {
+    const bool has_b = tile + 1 < n_tiles;
     resolve_blocks(tile + 2, ba);
     if (has_b) load_tile(tile + 1, bb, rb);
     process_tile(ra);
     resolve_blocks(tile + 3, bb);
-    if (tile + 2 < tile_end) load_tile(tile + 2, ba, ra);
+    if (tile + 2 < n_tiles) load_tile(tile + 2, ba, ra);
     if (has_b) process_tile(rb);
   }
 
