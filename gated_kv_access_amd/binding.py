@@ -21,7 +21,7 @@ BF16, F32, FP8_E4M3 = 0, 1, 2
 LAYER_GATED, LAYER_SLIDING = 0, 1
 ACCT_FIELDS = ("steps", "full_calls", "f_local", "f_full_taken", "f_full_always",
                "delta_f", "kv_bytes", "f_recall")
-DEVERR_CAPACITY, DEVERR_BLOCK_ID, DEVERR_OUT_CAPACITY = 1, 2, 4
+DEVERR_CAPACITY, DEVERR_BLOCK_ID, DEVERR_OUT_CAPACITY, DEVERR_MERGE_WAIT = 1, 2, 4, 8
 
 # Every symbol include/oda.h declares.
 EXPORTS = ("oda_workspace_size", "oda_workspace_init", "oda_prefill_kv", "oda_ring_init",

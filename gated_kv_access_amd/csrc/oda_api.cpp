@@ -110,25 +110,25 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
     if (f > units) f = units;
     if (f > kMaxSplits) f = kMaxSplits;
     p->full_splits = f < 1 ? 1 : f;
-    // Ring passes: one tile per workgroup while the (request, KV head) pairs
-    // leave the chip unfilled; at larger batches a single round of workgroups,
-    // each taking several tiles, so that no workgroup's fixed cost is paid twice
-    // per CU.
-    const int32_t rtiles = ceil_div(p->ring_slots + 1, p->ring_tile_rows);
+    // Ring passes: a single round of workgroups.  While the (request, KV head)
+    // pairs leave the chip unfilled, each pair spreads over ceil(256 / pairs)
+    // workgroups, which then hold less than a tile (the kernel skips the empty
+    // passes, so each SIMD reduces fewer rows); at larger batches each
+    // workgroup takes several tiles, so that no workgroup's fixed cost is paid
+    // twice per CU.
     const int32_t runits = ceil_div(p->ring_slots + 1, kSplitRowUnit);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
-    int32_t l = d->local_splits > 0 ? d->local_splits : (round < rtiles ? round : rtiles);
+    int32_t l = d->local_splits > 0 ? d->local_splits : round;
     if (l > runits) l = runits;
     if (l > kMaxSplits) l = kMaxSplits;
     p->local_splits = l < 1 ? 1 : l;
   }
   if (p->Ls > 0) {
-    const int32_t stiles = ceil_div(p->sw_window + 1, p->ring_tile_rows);
     const int32_t sunits = ceil_div(p->sw_window + 1, kSplitRowUnit);
     const int64_t pairs = (int64_t)b * p->Hkv;
     const int32_t round = pairs >= kComputeUnits ? 1 : (int32_t)ceil_div(kComputeUnits, pairs);
-    int32_t s = d->local_splits > 0 ? d->local_splits : (round < stiles ? round : stiles);
+    int32_t s = d->local_splits > 0 ? d->local_splits : round;
     if (s > sunits) s = sunits;
     if (s > kMaxSplits) s = kMaxSplits;
     p->sw_splits = s < 1 ? 1 : s;
@@ -149,7 +149,8 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
   w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
   w.commit_ticket_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
-  w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
+  w.flag_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
+  w.part_o_off = up(w.flag_off + sizeof(int32_t) * (size_t)b * p.Hkv * ms);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
   w.total = up(w.part_ml_off + sizeof(float) * 2 * (size_t)b * p.Hq * ms);
   return w;
@@ -253,6 +254,10 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
   a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
+  a.flags = reinterpret_cast<int32_t*>(c.base + c.ws.flag_off);
+  // Flags need every workgroup of the launch resident at once (the merging
+  // workgroup waits for the others): one per compute unit at most.
+  a.merge_mode = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits ? oda::kMergeFlags : oda::kMergeTicket;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;

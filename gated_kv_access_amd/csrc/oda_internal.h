@@ -37,7 +37,8 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
+  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, flag_off, part_o_off, part_ml_off,
+      total;
   int32_t max_splits;
 };
 
@@ -56,8 +57,15 @@ enum GateMode : int32_t {
   kGateBallot = 2,  // the pass compacts score > theta itself (standalone gated call)
 };
 
-// One attention pass of one layer: split-K partials, then the last workgroup
-// of each (request, KV head) merges them with the current token.
+// How the workgroup that merges a (request, KV head) is found.
+enum MergeMode : int32_t {
+  kMergeTicket = 0,  // the last to take a ticket (any launch size)
+  kMergeFlags = 1,   // the highest split, once the others' flags are up (every
+                     // workgroup of the launch resident at once)
+};
+
+// One attention pass of one layer: split-K partials, then one workgroup of
+// each (request, KV head) merges them.
 struct AttnParams {
   RowSpec rows;
   int32_t gate_mode;
@@ -84,6 +92,8 @@ struct AttnParams {
   float* part_o;              // [batch][Hq][splits][d]
   float* part_ml;             // [batch][Hq][splits][2]
   int32_t* tickets;           // [batch][Hkv], zero between launches
+  int32_t* flags;             // [batch][Hkv][splits], zero between launches
+  int32_t merge_mode;         // MergeMode
   uint32_t* err;
   float scale_log2;           // softmax scale * k_scale * log2(e)
   float v_scale;              // applied to the merged output

@@ -380,6 +380,22 @@ __device__ void write_call_list(const AttnParams& P) {
 // ----------------------------------------------------------------------------
 // merge of the split partials (run by one workgroup)
 
+// Run by one whole wave: waits until flags[0..n) are all non-zero.  Bounded:
+// after about a second it sets ODA_DEVERR_MERGE_WAIT and returns false.
+constexpr int32_t kFlagSpinLimit = 1 << 20;
+__device__ bool wait_flags(const int32_t* flags, int32_t n, uint32_t* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int32_t spin = 0; spin < kFlagSpinLimit; ++spin) {
+    bool up = true;
+    for (int32_t i = lane; i < n; i += kWave)
+      up &= __hip_atomic_load(const_cast<int32_t*>(flags + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    if (__all(up)) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane == 0) atomicOr(err, (uint32_t)ODA_DEVERR_MERGE_WAIT);
+  return false;
+}
+
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
 // One thread per output element (h, e); a wave serves one head.  Partials
@@ -492,7 +508,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   const int32_t n_tiles = (row_end - row_begin + TILE - 1) / TILE;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LPR;
   const int rrow = lane / LPR;
 
@@ -533,6 +549,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     uint4 k[NP][NV];
     uint4 v[NP][NV];
     bool valid[NP];  // paged: row in the pass; ring: row inside the ring (membership checked later)
+    bool live[NP];   // wave-uniform: the pass has rows of this split
     int32_t row[NP];
   };
   // Paged rows: the physical block of each lane's row, looked up two tiles
@@ -546,7 +563,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     for (int i = 0; i < NP; ++i) {
       B.blk[i] = -1;
       if constexpr (SRC == kSrcPaged) {
-        const int32_t row = row_begin + tile * TILE + (wave * NP + i) * RPP + rrow;
+        const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP + rrow;
         if (tile < n_tiles && row < row_end && row < n_rows) {
           const int32_t p = interval_position(iv, row);
           B.blk[i] = btab[(p - 1) >> P.block_shift];
@@ -557,8 +574,16 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int32_t row = row_begin + tile * TILE + (wave * NP + i) * RPP + rrow;
+      const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP + rrow;
       R.row[i] = row;
+      // Pass i of a tile covers rows i*8*RPP .. (i+1)*8*RPP-1 across the 8 waves, so
+      // a split shorter than a tile leaves whole passes empty in every wave and
+      // both waves of a SIMD skip them.
+      R.live[i] = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP < row_end;
+      if (!R.live[i]) {
+        R.valid[i] = false;
+        continue;
+      }
       bool ok = row < row_end;  // row_end <= n_rows + 1
       const char* kb = kbase;
       const char* vb = vbase;
@@ -601,6 +626,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       // yet written may hold anything, so their values are replaced by zeros).
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
+        if (!R.live[i]) continue;
         bool in_local = R.valid[i] && R.row[i] == n_rows;  // the current token
         if (R.valid[i] && !in_local) ring_slot_position(rst, R.row[i], in_local);
         R.valid[i] = in_local;
@@ -613,6 +639,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     float s[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+      if (!R.live[i]) continue;
       // FP8 keys become bf16 pairs once per row, shared by the G heads.
       uint32_t kb[DT == ODA_FP8_E4M3 ? 2 * 4 * NV : 1];
       if constexpr (DT == ODA_FP8_E4M3) {
@@ -664,6 +691,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // only when a score would push a weight past 2^kRescaleGap.
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+      if (!R.live[i]) continue;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (s[i][h] > m_run[h] + kRescaleGap) {
@@ -679,6 +707,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // p = exp2(s - m); o += p * v
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+      if (!R.live[i]) continue;
       float pr[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -828,22 +857,46 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
   }
 
-  // The last workgroup of this (request, KV head) to finish merges.  Every
-  // wave waits until its device-scope partial stores have completed, then one
-  // thread takes a ticket; the holder of the last ticket reads all partials
-  // with device-scope loads.
+  // Completion.  Every wave first waits until its device-scope partial stores
+  // have completed.
+  const int64_t pair = (int64_t)b * P.Hkv + g;
+  if (P.merge_mode == kMergeFlags) {
+    // Every workgroup of the launch is resident: the highest split merges
+    // once the others have raised their flags; no read-modify-write on a
+    // shared counter, whose same-address atomics serialise.
+    int32_t* flags = P.flags + pair * P.splits;
+    if (split + 1 < used) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // Wave 0 polls the flags while this workgroup's own stores complete.
+    if (wave == 0) {
+      const bool ok = wait_flags(flags, used - 1, P.err);
+      if (lane == 0) s_last = ok;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!s_last) return;
+    merge_and_write<DT, D, G>(P, b, g, used);
+    for (int32_t i = threadIdx.x; i < used - 1; i += kGroupThreads)  // ready for the next launch
+      __hip_atomic_store(flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  // Any launch size: the last workgroup of this (request, KV head) to take a
+  // ticket reads all partials with device-scope loads.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int32_t prev = __hip_atomic_fetch_add(&P.tickets[(int64_t)b * P.Hkv + g], 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t prev = __hip_atomic_fetch_add(&P.tickets[pair], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == used - 1;
   }
   __syncthreads();
   if (!s_last) return;
   merge_and_write<DT, D, G>(P, b, g, used);
   if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
-    __hip_atomic_store(&P.tickets[(int64_t)b * P.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.tickets[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------

@@ -70,8 +70,13 @@ typedef enum { ODA_LAYER_GATED = 0, ODA_LAYER_SLIDING = 1 } oda_layer_kind;
 
 enum { ODA_MAX_LAYERS = 256, ODA_MAX_BATCH = 4096 };
 
-/* Bits of the device error word (first 4 bytes of the workspace). */
-enum { ODA_DEVERR_CAPACITY = 1, ODA_DEVERR_BLOCK_ID = 2, ODA_DEVERR_OUT_CAPACITY = 4 };
+/* Bits of the device error word (first 4 bytes of the workspace).
+ * ODA_DEVERR_MERGE_WAIT: in a launch small enough for all its workgroups to be
+ * resident at once, the workgroup that merges a (request, KV head) gave up
+ * waiting (about a second) for the other splits, e.g. because other work held
+ * the compute units; that pass's outputs are not written and the workspace
+ * must be zeroed again (oda_workspace_init) before further use. */
+enum { ODA_DEVERR_CAPACITY = 1, ODA_DEVERR_BLOCK_ID = 2, ODA_DEVERR_OUT_CAPACITY = 4, ODA_DEVERR_MERGE_WAIT = 8 };
 
 /* Accounting counters, int64 per request (see oda_gate). */
 enum {
