@@ -149,10 +149,10 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
   w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
   w.commit_ticket_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
-  w.flag_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
-  w.part_o_off = up(w.flag_off + sizeof(int32_t) * (size_t)b * p.Hkv * ms);
+  w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
-  w.total = up(w.part_ml_off + sizeof(float) * 2 * (size_t)b * p.Hq * ms);
+  const size_t ml_copies = p.D >= 64 ? (size_t)p.D / 64 : 1;  // one (m, l) per merging wave
+  w.total = up(w.part_ml_off + sizeof(float) * 2 * ml_copies * (size_t)b * p.Hq * ms);
   return w;
 }
 
@@ -254,10 +254,9 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
   a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
-  a.flags = reinterpret_cast<int32_t*>(c.base + c.ws.flag_off);
-  // Flags need every workgroup of the launch resident at once (the merging
+  // Polling needs every workgroup of the launch resident at once (the merging
   // workgroup waits for the others): one per compute unit at most.
-  a.merge_mode = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits ? oda::kMergeFlags : oda::kMergeTicket;
+  a.merge_mode = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits ? oda::kMergePoll : oda::kMergeTicket;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
@@ -346,7 +345,7 @@ oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspa
   Ctx c;
   oda_status st = prepare(dims, batch, workspace, bytes, &c);
   if (st != ODA_OK) return st;
-  return hip_status(oda::launch_clear(workspace, c.ws.total, stream));
+  return hip_status(oda::launch_workspace_init(workspace, c.ws.part_o_off, c.ws.total, stream));
 }
 
 oda_status oda_prefill_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch, int32_t layer,

@@ -37,8 +37,7 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, flag_off, part_o_off, part_ml_off,
-      total;
+  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
   int32_t max_splits;
 };
 
@@ -60,8 +59,9 @@ enum GateMode : int32_t {
 // How the workgroup that merges a (request, KV head) is found.
 enum MergeMode : int32_t {
   kMergeTicket = 0,  // the last to take a ticket (any launch size)
-  kMergeFlags = 1,   // the highest split, once the others' flags are up (every
-                     // workgroup of the launch resident at once)
+  kMergePoll = 1,    // the highest split, reading the others' partial slots
+                     // until none is empty (every workgroup of the launch
+                     // resident at once)
 };
 
 // One attention pass of one layer: split-K partials, then one workgroup of
@@ -90,9 +90,8 @@ struct AttnParams {
   float* out;                 // [batch][Hq][d]
   float* lse;                 // [batch][Hq] or NULL
   float* part_o;              // [batch][Hq][splits][d]
-  float* part_ml;             // [batch][Hq][splits][2]
+  float* part_ml;             // [batch][Hq][splits][d / 64][2]  (one copy per merging wave)
   int32_t* tickets;           // [batch][Hkv], zero between launches
-  int32_t* flags;             // [batch][Hkv][splits], zero between launches
   int32_t merge_mode;         // MergeMode
   uint32_t* err;
   float scale_log2;           // softmax scale * k_scale * log2(e)
@@ -114,6 +113,9 @@ int launch_access_set(const Plan& p, const oda_kv& kv, int32_t layer, int32_t b,
                       int32_t* positions, int64_t capacity, int64_t* count, uint32_t* err,
                       oda_stream s);
 int launch_clear(void* ptr, size_t bytes, oda_stream s);
+// Zeroes workspace bytes [0, partials_off) and marks the split partials at
+// [partials_off, total) empty.
+int launch_workspace_init(void* ws, size_t partials_off, size_t total, oda_stream s);
 int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,
                  int64_t* counter, int64_t num_steps, oda_stream s);
 int launch_advance(int64_t* counter, oda_stream s);

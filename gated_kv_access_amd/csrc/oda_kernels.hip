@@ -380,55 +380,81 @@ __device__ void write_call_list(const AttnParams& P) {
 // ----------------------------------------------------------------------------
 // merge of the split partials (run by one workgroup)
 
-// Run by one whole wave: waits until flags[0..n) are all non-zero.  Bounded:
-// after about a second it sets ODA_DEVERR_MERGE_WAIT and returns false.
-constexpr int32_t kFlagSpinLimit = 1 << 20;
-__device__ bool wait_flags(const int32_t* flags, int32_t n, uint32_t* err) {
-  const int lane = threadIdx.x & (kWave - 1);
-  for (int32_t spin = 0; spin < kFlagSpinLimit; ++spin) {
-    bool up = true;
-    for (int32_t i = lane; i < n; i += kWave)
-      up &= __hip_atomic_load(const_cast<int32_t*>(flags + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    if (__all(up)) return true;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  if (lane == 0) atomicOr(err, (uint32_t)ODA_DEVERR_MERGE_WAIT);
-  return false;
-}
+// A partial slot reads kPartialEmpty (a signalling NaN, which no arithmetic
+// result ever is) from the moment a merge has consumed it until a workgroup
+// of a later launch stores its partial there.  The merging workgroup of a
+// launch whose workgroups are all resident at once therefore needs no flag or
+// counter: it reads the slots and reads again those still empty.
+constexpr uint32_t kPartialEmpty = 0x7FA5A5A5u;
+constexpr int32_t kMergeSpinLimit = 1 << 20;  // about a second of re-reads
+__device__ __forceinline__ bool slot_empty(float x) { return __float_as_uint(x) == kPartialEmpty; }
 
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
 // One thread per output element (h, e); a wave serves one head.  Partials
-// are taken in rounds of up to kMergeBatch: lane i loads (m, l) of partial i
-// of the round (one 8-byte load), every lane loads its element of each
-// partial's o, the round's maximum and weights come from lane exchanges, and
-// the weights reach every lane by lane reads.  The current token is a row of
-// the last split, so only partials are combined here.  No LDS, no barrier.
+// 0..n_mem-1 are read from the workspace in rounds of up to kMergeBatch:
+// lane i loads (m, l) of partial i of the round (one 8-byte load), every lane
+// loads its element of each partial's o, the round's maximum and weights come
+// from lane exchanges, and the weights reach every lane by lane reads.  With
+// `poll`, a round is read again (by the whole wave) while any of its values is
+// still empty.  `own_o` / `own_ml` (LDS, may be null) is one more partial,
+// the merging workgroup's own.  Each round's slots are left empty for the
+// next launch as soon as they are read.  Returns false (and sets ODA_DEVERR_MERGE_WAIT) if polling gives up.
+// No LDS writes, no barrier.
 template <int DT, int D, int G>
-__device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t used) {
+__device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
+                                const float* own_o, const float* own_ml) {
   constexpr int GD = G * D;
   static_assert(GD <= kGroupThreads && D % kWave == 0, "one thread per output, one head per wave");
   const int tid = threadIdx.x;
-  if (tid >= GD) return;
+  if (tid >= GD) return true;
   const int lane = tid & (kWave - 1);
   const int h = tid / D, e = tid % D;
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
-  const float* ml = P.part_ml + (head0 + h) * P.splits * 2;
-  const float* po = P.part_o + (head0 + h) * P.splits * D + e;
+  // (m, l) is stored once per wave of a head (D / 64 copies), so each wave
+  // reads, checks and empties its own copy.
+  constexpr int kCopies = D / kWave;
+  const int half = e / kWave;
+  float* ml = P.part_ml + (head0 + h) * P.splits * 2 * kCopies + 2 * half;
+  float* po = P.part_o + (head0 + h) * P.splits * D + e;
+  const float empty = __uint_as_float(kPartialEmpty);
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int32_t base = 0; base < used; base += kMergeBatch) {
-    const int32_t n = used - base < kMergeBatch ? used - base : kMergeBatch;
+  for (int32_t base = 0; base < n_mem; base += kMergeBatch) {
+    const int32_t n = n_mem - base < kMergeBatch ? n_mem - base : kMergeBatch;
     // Branch-free: slots past the round's end re-read its last partial (their
     // weights are zero below), so all loads leave back to back.
     float x[kMergeBatch];
+    float mi, li;
+    for (int32_t spin = 0;; ++spin) {
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) x[i] = collect(po + (int64_t)(base + (i < n ? i : n - 1)) * D);
-    float mi = -INFINITY, li = 0.f;
-    if (lane < n) {
-      const uint64_t w2 = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(ml + 2 * (base + lane))),
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      mi = __uint_as_float((uint32_t)w2);
-      li = __uint_as_float((uint32_t)(w2 >> 32));
+      for (int i = 0; i < kMergeBatch; ++i) x[i] = collect(po + (int64_t)(base + (i < n ? i : n - 1)) * D);
+      mi = -INFINITY;
+      li = 0.f;
+      if (lane < n) {
+        const uint64_t w2 = __hip_atomic_load(reinterpret_cast<uint64_t*>(ml + 2 * kCopies * (base + lane)),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mi = __uint_as_float((uint32_t)w2);
+        li = __uint_as_float((uint32_t)(w2 >> 32));
+      }
+      if (!poll) break;
+      bool missing = slot_empty(mi) || slot_empty(li);
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) missing = missing || slot_empty(x[i]);
+      if (!__any(missing)) break;
+      if (spin == kMergeSpinLimit) {
+        if (lane == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_MERGE_WAIT);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    {
+      // The round's slots are read: this wave leaves what it read empty for the
+      // next launch (plain 16-byte stores; the launch boundary publishes them):
+      // its 64 elements of each of the n rows of o, and its copy of (m, l).
+      float4* ro = reinterpret_cast<float4*>(P.part_o + ((head0 + h) * P.splits + base) * D) + half * (kWave / 4);
+      const float4 e4 = make_float4(empty, empty, empty, empty);
+      for (int32_t i = lane; i < n * (kWave / 4); i += kWave) ro[(i / (kWave / 4)) * (D / 4) + i % (kWave / 4)] = e4;
+      if (lane < n) *reinterpret_cast<float2*>(ml + 2 * kCopies * (base + lane)) = make_float2(empty, empty);
     }
     const float m_new = fmaxf(M, max_over<1, 32>(mi));
     const float keep = M == -INFINITY ? 0.f : fast_exp2(M - m_new);
@@ -440,8 +466,18 @@ __device__ void merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
       acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], acc);
     M = m_new;
   }
+  if (own_o != nullptr) {
+    const float mo = own_ml[2 * h], lo = own_ml[2 * h + 1];
+    const float m_new = fmaxf(M, mo);
+    const float keep = M == -INFINITY ? 0.f : fast_exp2(M - m_new);
+    const float wo = mo == -INFINITY ? 0.f : fast_exp2(mo - m_new);
+    L = fmaf(L, keep, wo * lo);
+    acc = fmaf(acc, keep, wo * own_o[tid]);
+    M = m_new;
+  }
   P.out[(head0 + h) * D + e] = acc / L * P.v_scale;
   if (P.lse != nullptr && e == 0) P.lse[head0 + h] = (M + __log2f(L)) * kLn2;
+  return true;
 }
 
 // ----------------------------------------------------------------------------
@@ -830,6 +866,14 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
               make_float4(o[h][j * EPV + c], o[h][j * EPV + c + 1], o[h][j * EPV + c + 2], o[h][j * EPV + c + 3]);
   }
   __syncthreads();
+  // Poll mode (the host uses it when every workgroup of the launch is resident
+  // at once): the highest split merges and keeps its own partial in LDS; the
+  // others store theirs and leave.  Ticket mode: every split stores its
+  // partial and the last to take a ticket merges.
+  const bool poll = P.merge_mode == kMergePoll;
+  const bool merges_here = poll && split + 1 == used;
+  __shared__ float s_own_o[G * D];
+  __shared__ float s_own_ml[G][2];
   // TPO adjacent threads share an output and add NWR / TPO rows each.
   constexpr int TPO = G * D >= kGroupThreads ? 1 : (kGroupThreads / (G * D) >= 4 ? 4 : kGroupThreads / (G * D));
   static_assert(TPO == 1 || TPO == 2 || TPO == 4, "threads per output");
@@ -843,7 +887,10 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if constexpr (TPO >= 4) acc += xor_lane<2>(acc);
     if (part != 0) continue;
     const int64_t row = ((int64_t)b * P.Hq + (int64_t)g * G + h) * P.splits + split;
-    publish(P.part_o + row * D + e, acc);
+    if (merges_here)
+      s_own_o[out_i] = acc;
+    else
+      publish(P.part_o + row * D + e, acc);
     if (e == 0) {
       float lsum = 0.f;
 #pragma unroll
@@ -852,40 +899,29 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
       for (int hh = 1; hh < G; ++hh)
         if (hh == h) mh = M[hh];
-      publish(P.part_ml + row * 2 + 0, mh);
-      publish(P.part_ml + row * 2 + 1, lsum);
+      if (merges_here) {
+        s_own_ml[h][0] = mh;
+        s_own_ml[h][1] = lsum;
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / kWave; ++c) {  // one copy per merging wave
+          publish(P.part_ml + (row * (D / kWave) + c) * 2 + 0, mh);
+          publish(P.part_ml + (row * (D / kWave) + c) * 2 + 1, lsum);
+        }
+      }
     }
   }
 
-  // Completion.  Every wave first waits until its device-scope partial stores
-  // have completed.
-  const int64_t pair = (int64_t)b * P.Hkv + g;
-  if (P.merge_mode == kMergeFlags) {
-    // Every workgroup of the launch is resident: the highest split merges
-    // once the others have raised their flags; no read-modify-write on a
-    // shared counter, whose same-address atomics serialise.
-    int32_t* flags = P.flags + pair * P.splits;
-    if (split + 1 < used) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    // Wave 0 polls the flags while this workgroup's own stores complete.
-    if (wave == 0) {
-      const bool ok = wait_flags(flags, used - 1, P.err);
-      if (lane == 0) s_last = ok;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (poll) {
+    if (!merges_here) return;
     __syncthreads();
-    if (!s_last) return;
-    merge_and_write<DT, D, G>(P, b, g, used);
-    for (int32_t i = threadIdx.x; i < used - 1; i += kGroupThreads)  // ready for the next launch
-      __hip_atomic_store(flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0]);
     return;
   }
-  // Any launch size: the last workgroup of this (request, KV head) to take a
-  // ticket reads all partials with device-scope loads.
+  // Ticket mode: every wave waits until its device-scope partial stores have
+  // completed, then one thread takes a ticket; the holder of the last ticket
+  // reads all partials.
+  const int64_t pair = (int64_t)b * P.Hkv + g;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -894,7 +930,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
   __syncthreads();
   if (!s_last) return;
-  merge_and_write<DT, D, G>(P, b, g, used);
+  merge_and_write<DT, D, G>(P, b, g, used, false, nullptr, nullptr);
   if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1243,9 +1279,9 @@ __global__ __launch_bounds__(256) void access_set_kernel(AccessParams P) {
 // ----------------------------------------------------------------------------
 // small helpers
 
-__global__ void clear_kernel(uint32_t* p, int64_t words) {
+__global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t value) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+    p[i] = value;
 }
 
 struct StageParams {
@@ -1511,13 +1547,19 @@ int launch_access_set(const Plan& p, const oda_kv& kv, int32_t layer, int32_t b,
   return (int)hipGetLastError();
 }
 
-int launch_clear(void* ptr, size_t bytes, oda_stream s) {
+int launch_fill(void* ptr, size_t bytes, uint32_t value, oda_stream s) {
   const int64_t words = (int64_t)(bytes / 4);
   if (words <= 0) return 0;
   int64_t blocks = (words + 255) / 256;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(ptr), words);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t*>(ptr), words, value);
   return (int)hipGetLastError();
+}
+int launch_clear(void* ptr, size_t bytes, oda_stream s) { return launch_fill(ptr, bytes, 0u, s); }
+int launch_workspace_init(void* ws, size_t partials_off, size_t total, oda_stream s) {
+  const int e = launch_fill(ws, partials_off, 0u, s);
+  if (e != 0) return e;
+  return launch_fill(static_cast<char*>(ws) + partials_off, total - partials_off, kPartialEmpty, s);
 }
 
 int launch_stage(int32_t n, const void* const* src, void* const* dst, const int64_t* bytes,

@@ -75,7 +75,7 @@ enum { ODA_MAX_LAYERS = 256, ODA_MAX_BATCH = 4096 };
  * resident at once, the workgroup that merges a (request, KV head) gave up
  * waiting (about a second) for the other splits, e.g. because other work held
  * the compute units; that pass's outputs are not written and the workspace
- * must be zeroed again (oda_workspace_init) before further use. */
+ * must be prepared again (oda_workspace_init) before further use. */
 enum { ODA_DEVERR_CAPACITY = 1, ODA_DEVERR_BLOCK_ID = 2, ODA_DEVERR_OUT_CAPACITY = 4, ODA_DEVERR_MERGE_WAIT = 8 };
 
 /* Accounting counters, int64 per request (see oda_gate). */
@@ -139,10 +139,13 @@ typedef struct {
  * first 256 bytes hold the device error word).  0 on invalid dims. */
 size_t oda_workspace_size(const oda_dims* dims, int32_t batch);
 
-/* Zeroes the workspace (a small kernel; call once after allocating it).  The
- * kernels keep ticket words there that must read zero between launches (they
- * find the last workgroup of a request with them and reset them), next to the
- * error word and the split partials. */
+/* Prepares the workspace (small kernels; call once after allocating it): zeroes
+ * the error word and the ticket words, and marks every split-partial slot
+ * empty.  Between launches the tickets read zero and the slots read empty:
+ * each launch's merging workgroup finds the other splits' partials by a ticket
+ * (any launch size) or by re-reading slots until none is empty (launches
+ * whose workgroups are all resident at once), and leaves both as it found
+ * them. */
 oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspace,
                               size_t workspace_bytes, oda_stream stream);
 
