@@ -13,7 +13,7 @@ import torch
 import oracle as orc
 from gated_kv_access_amd import binding as B
 from gated_kv_access_amd import workloads as W
-from gated_kv_access_amd.state import DecodeState
+from gated_kv_access_amd.state import DecodeState, make_dims
 from tests.gpu_helpers import (assert_outputs_close, oracle_cfg, oracle_sequences, run_steps, say,
                                words, LSE_TOL)
 
@@ -38,9 +38,9 @@ SMALL = [
 ]
 
 
-def _check_run(wl, graph=False, q_full=False, host_cache=False):
+def _check_run(wl, graph=False, q_full=False, host_cache=False, dims=None):
     say(f"{wl.name}: prefill {wl.prefill}, {wl.steps} steps, graph={graph}, host_cache={host_cache}")
-    st = DecodeState(wl, gen_device="cpu", host_cache=host_cache)
+    st = DecodeState(wl, gen_device="cpu", host_cache=host_cache, dims=dims)
     st.prefill()
     q = W.gen_queries(wl, "cpu")
     qf = W.gen_queries(wl, "cpu", tag=4) if q_full else None
@@ -261,6 +261,34 @@ def test_gate_and_accounting_bit_exact():
 
 
 # ---------------------------------------------------------------- standalone per-layer calls
+
+EMPTY_SLOT = 0x7FA5A5A5  # what an unused split-partial word of the workspace holds
+
+
+def _empty_words(st) -> int:
+    torch.cuda.synchronize()
+    return int((st.workspace.cpu().numpy().view(np.uint32) == EMPTY_SLOT).sum())
+
+
+@pytest.mark.parametrize("full_splits,local_splits", [(50, 17), (24, 48), (50, 48)],
+                         ids=["full_ticket", "local_ticket", "both_ticket"])
+def test_ticket_and_polling_merges_share_one_workspace(full_splits, local_splits):
+    """A launch whose workgroups all fit on the chip at once (at most 256)
+    merges by re-reading the partial slots until none is empty; a larger one by
+    the last ticket.  With batch 3 and 2 KV heads, 50 or 48 splits make the
+    Full or the Local passes take tickets while the other kind polls, on the
+    same partial slots.  Outputs match the oracle, and after every step each
+    partial word of the workspace reads empty again (as after initialisation)."""
+    wl = _small("merge_modes", window=1024, steps=6, seed=171)
+    dims = make_dims(wl, full_splits=full_splits, local_splits=local_splits)
+    ms = max(full_splits, local_splits)
+    slots = wl.batch * wl.num_q_heads * ms * (wl.head_dim + 2 * (wl.head_dim // 64))
+    st = DecodeState(wl, gen_device="cpu", dims=dims)
+    at_init = _empty_words(st)
+    assert slots <= at_init < slots + 128  # plus the padding that aligns the partial arrays
+    st, got, want = _check_run(wl, dims=dims)
+    assert _empty_words(st) == at_init
+
 
 def test_standalone_local_and_gated_full_calls():
     wl = _small("standalone", prefill=(0, 1200, 2600), steps=1, seed=151)
