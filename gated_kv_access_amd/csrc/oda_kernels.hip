@@ -504,7 +504,11 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
 // ----------------------------------------------------------------------------
 // one attention pass of one layer: split-K partials + last-workgroup merge
 
-template <int DT, int D, int G, int SRC, bool BALLOT>
+// SKIP: passes without rows of this split are skipped by wave-uniform branches
+// (the host asks for it when the splits are shorter than a tile, and for paged
+// passes).  Without it, a ring pass that loops over many tiles keeps its loads
+// in flight across the joins.
+template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
   using Gm = Geo<DT, D, SRC>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
@@ -636,10 +640,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       // Pass i of a tile covers rows i*8*RPP .. (i+1)*8*RPP-1 across the 8 waves, so
       // a split shorter than a tile leaves whole passes empty in every wave and
       // both waves of a SIMD skip them.
-      R.live[i] = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP < row_end;
-      if (!R.live[i]) {
-        R.valid[i] = false;
-        continue;
+      if constexpr (SKIP) {
+        R.live[i] = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP < row_end;
+        if (!R.live[i]) {
+          R.valid[i] = false;
+          continue;
+        }
       }
       bool ok = row < row_end;  // row_end <= n_rows + 1
       const char* kb = kbase;
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       // yet written may hold anything, so their values are replaced by zeros).
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        if (!R.live[i]) continue;
+        if (SKIP && !R.live[i]) continue;
         bool in_local = R.valid[i] && R.row[i] == n_rows;  // the current token
         if (R.valid[i] && !in_local) ring_slot_position(rst, R.row[i], in_local);
         R.valid[i] = in_local;
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     float s[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (!R.live[i]) continue;
+      if (SKIP && !R.live[i]) continue;
       // FP8 keys become bf16 pairs once per row, shared by the G heads.
       uint32_t kb[DT == ODA_FP8_E4M3 ? 2 * 4 * NV : 1];
       if constexpr (DT == ODA_FP8_E4M3) {
@@ -748,7 +754,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // only when a score would push a weight past 2^kRescaleGap.
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (!R.live[i]) continue;
+      if (SKIP && !R.live[i]) continue;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (s[i][h] > m_run[h] + kRescaleGap) {
@@ -764,7 +770,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // p = exp2(s - m); o += p * v
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (!R.live[i]) continue;
+      if (SKIP && !R.live[i]) continue;
       float pr[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -1439,12 +1445,21 @@ template <int DT, int D, int G>
 int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   dim3 grid(a.splits, a.Hkv, batch);
   const bool ballot = a.gate_mode == kGateBallot;
+  const dim3 block(kGroupThreads);
   if (a.rows.source == kSrcRing) {
-    if (ballot) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true>), grid, dim3(kGroupThreads), 0, s, a);
-    else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, false>), grid, dim3(kGroupThreads), 0, s, a);
+    // Splits no longer than a tile (the usual case at small batch) skip empty passes.
+    const int32_t units = (a.rows.ring_slots + 1 + kSplitRowUnit - 1) / kSplitRowUnit;
+    const bool skip = (int64_t)((units + a.splits - 1) / a.splits) * kSplitRowUnit <= Geo<DT, D, kSrcRing>::TILE;
+    if (ballot) {
+      if (skip) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true, false>), grid, block, 0, s, a);
+    } else {
+      if (skip) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, false, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, false, false>), grid, block, 0, s, a);
+    }
   } else {
-    if (ballot) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, true>), grid, dim3(kGroupThreads), 0, s, a);
-    else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, false>), grid, dim3(kGroupThreads), 0, s, a);
+    if (ballot) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcPaged, false, true>), grid, block, 0, s, a);
   }
   return (int)hipGetLastError();
 }
