@@ -832,12 +832,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (has_b) process_tile(rb);
   }
 
-  constexpr int kRows16 = kWave / 16;
-  constexpr int NWR = kWavesPerGroup * kRows16;
-  // Rows of the LDS fold: one per wave (wide geometry), else one per 16-lane row.
-  constexpr int FOLD_ROWS = Gm::WIDE ? kWavesPerGroup : NWR;
+  constexpr int FOLD_ROWS = kWavesPerGroup;  // rows of the LDS fold: one per wave
   __shared__ float s_wmax[kWavesPerGroup][G];
-  constexpr int RS = G * D + 4;  // LDS row stride: the four 16-lane rows of a wave store to distinct banks
+  constexpr int RS = G * D + 4;  // LDS row stride (words)
   __shared__ float s_o[FOLD_ROWS][RS];
   __shared__ float s_l[kWavesPerGroup][G];
   __shared__ int32_t s_last;
@@ -874,11 +871,11 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   constexpr int TPO = G * D >= kGroupThreads ? 1 : (kGroupThreads / (G * D) >= 4 ? 4 : kGroupThreads / (G * D));
   static_assert(TPO == 1 || TPO == 2 || TPO == 4, "threads per output");
 
-  if constexpr (Gm::WIDE) {
-    // Epilogue, wide geometry (one barrier): each wave rescales its row groups
-    // onto the wave's maximum per head, adds them (DPP inside 16-lane rows,
-    // row swaps across them) and stores one LDS row with its (m, l); the fold
-    // weighs the 8 wave rows by 2^(m_w - M).
+  {
+    // Epilogue (one barrier): each wave rescales its row groups onto the
+    // wave's maximum per head, adds them (DPP inside 16-lane rows, row swaps
+    // across them) and stores one LDS row with its (m, l); the fold weighs the
+    // 8 wave rows by 2^(m_w - M).
     constexpr int V = G * EPL;
     float v[V];
 #pragma unroll
@@ -905,15 +902,18 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
     float u[V / 4];
     wave_rows_sum_spread<V>(v, u);
-    // Lane quarter q holds values q*V/4 .. of its column: runs of RUN elements
-    // of one head, contiguous in the output row.
-    constexpr int RUN = V / 4 < EPL ? V / 4 : EPL;
+    // Lane quarter q holds values q*V/4 .. of its column (value h*EPL + e is
+    // element (e / EPV * LPR + col) * EPV + e % EPV of head h): runs of RUN
+    // elements, contiguous in the output row.  With LPR < 16 the lanes of a
+    // 16-lane row past the first LPR hold copies.
+    constexpr int RUN = V / 4 < EPV ? V / 4 : EPV;
     const int q = lane >> 4, col = lane & 15;
     if (col < LPR) {
 #pragma unroll
       for (int k0 = 0; k0 < V / 4; k0 += RUN) {
         const int kk = q * (V / 4) + k0;
-        float* dst = &s_o[wave][(kk / EPL) * D + col * EPL + kk % EPL];
+        const int e = kk % EPL;
+        float* dst = &s_o[wave][(kk / EPL) * D + ((e / EPV) * LPR + col) * EPV + e % EPV];
         if constexpr (RUN % 4 == 0) {
 #pragma unroll
           for (int k = 0; k < RUN; k += 4)
@@ -948,83 +948,6 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
         for (int w = 0; w < kWavesPerGroup; ++w)
           lsum = fmaf(s_wmax[w][h] == -INFINITY ? 0.f : fast_exp2(s_wmax[w][h] - Mh), s_l[w][h], lsum);
         emit_ml(h, Mh, lsum);
-      }
-    }
-  } else {
-    // Epilogue, other geometries (two barriers).  1: the workgroup's maximum
-    // reference per head (DPP inside each
-    // 16-lane row, lane reads across the four rows, one LDS exchange between
-    // waves); every lane then rescales its sums onto it and the row groups of
-    // each 16-lane row are added with DPP.  The partials left for the LDS fold
-    // share one maximum, so the fold is a plain sum.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int mr = __float_as_int(row_group_max<LPR>(m_run[h]));
-      const float m4 = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mr, 0)),
-                                   __int_as_float(__builtin_amdgcn_readlane(mr, 16))),
-                             fmaxf(__int_as_float(__builtin_amdgcn_readlane(mr, 32)),
-                                   __int_as_float(__builtin_amdgcn_readlane(mr, 48))));
-      if (lane == 0) s_wmax[wave][h] = m4;
-    }
-    __syncthreads();
-    float M[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      M[h] = s_wmax[0][h];
-#pragma unroll
-      for (int w = 1; w < kWavesPerGroup; ++w) M[h] = fmaxf(M[h], s_wmax[w][h]);
-      const float sc = m_run[h] == -INFINITY ? 0.f : fast_exp2(m_run[h] - M[h]);
-      {
-#pragma clang fp contract(off)  // keep the scaling separate so each DPP move folds into an add
-        l_acc[h] = row_group_sum<LPR>(l_acc[h] * sc);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          o[h][e] = row_group_sum<LPR>(o[h][e] * sc);
-          asm volatile("" : "+v"(o[h][e]));  // the sums are complete here, not inside the store branch
-        }
-      }
-      // the wave's l: the four 16-lane rows' sums, read across lanes
-      const int li = __float_as_int(l_acc[h]);
-      const float lw = (__int_as_float(__builtin_amdgcn_readlane(li, 0)) + __int_as_float(__builtin_amdgcn_readlane(li, 16))) +
-                       (__int_as_float(__builtin_amdgcn_readlane(li, 32)) + __int_as_float(__builtin_amdgcn_readlane(li, 48)));
-      if (lane == 0) s_l[wave][h] = lw;
-    }
-
-    // Epilogue 2: the first LPR lanes of each 16-lane row hold distinct element
-    // slices; they store the row's sums, and after one barrier each output
-    // thread adds the 8 waves x 4 rows and publishes this workgroup's partial
-    // device-wide.
-    const int wr = wave * kRows16 + (lane >> 4);
-    if ((lane & 15) < LPR) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-#pragma unroll
-          for (int c = 0; c < EPV; c += 4)
-            *reinterpret_cast<float4*>(&s_o[wr][h * D + (j * LPR + sub) * EPV + c]) =
-                make_float4(o[h][j * EPV + c], o[h][j * EPV + c + 1], o[h][j * EPV + c + 2], o[h][j * EPV + c + 3]);
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D * TPO; idx += kGroupThreads) {
-      const int out_i = idx / TPO, part = idx % TPO;
-      const int h = out_i / D, e = out_i % D;
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < NWR / TPO; ++r) acc += s_o[part * (NWR / TPO) + r][out_i];
-      if constexpr (TPO >= 2) acc += xor_lane<1>(acc);
-      if constexpr (TPO >= 4) acc += xor_lane<2>(acc);
-      if (part != 0) continue;
-      emit_o(h, e, acc);
-      if (e == 0) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) lsum += s_l[w][h];
-        float mh = M[0];
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh)
-          if (hh == h) mh = M[hh];
-        emit_ml(h, mh, lsum);
       }
     }
   }
