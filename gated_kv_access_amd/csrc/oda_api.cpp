@@ -148,7 +148,8 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.list_off = oda::kWsHeader;
   w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
   w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
-  w.commit_ticket_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
+  w.claim_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
+  w.commit_ticket_off = up(w.claim_off + sizeof(int32_t) * (size_t)b * p.Hkv);
   w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
   const size_t ml_copies = p.D >= 64 ? (size_t)p.D / 64 : 1;  // one (m, l) per merging wave
@@ -254,6 +255,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
   a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
+  a.claims = reinterpret_cast<int32_t*>(c.base + c.ws.claim_off);
   // Polling needs every workgroup of the launch resident at once (the merging
   // workgroup waits for the others): one per compute unit at most.
   a.merge_mode = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits ? oda::kMergePoll : oda::kMergeTicket;

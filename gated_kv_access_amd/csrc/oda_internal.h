@@ -37,7 +37,8 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, len_off, ticket_off, commit_ticket_off, part_o_off, part_ml_off, total;
+  size_t err_off, count_off, list_off, len_off, ticket_off, claim_off, commit_ticket_off, part_o_off, part_ml_off,
+      total;
   int32_t max_splits;
 };
 
@@ -92,6 +93,7 @@ struct AttnParams {
   float* part_o;              // [batch][Hq][splits][d]
   float* part_ml;             // [batch][Hq][splits][d / 64][2]  (one copy per merging wave)
   int32_t* tickets;           // [batch][Hkv], zero between launches
+  int32_t* claims;            // [batch][Hkv], zero between launches: pool tiles taken (paged passes)
   int32_t merge_mode;         // MergeMode
   uint32_t* err;
   float scale_log2;           // softmax scale * k_scale * log2(e)

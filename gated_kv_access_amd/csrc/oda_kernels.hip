@@ -561,8 +561,18 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
   // Row n_rows is the current token t, read from k_cur / v_cur: it is
   // processed like any other row, by the last split.
+  // Paged passes over long ranges keep a pool of tail tiles, 2 per split, at
+  // the end of the range: the splits divide rows [0, n_static) statically and
+  // then take pool tiles one at a time from a per-(request, KV head) counter,
+  // so workgroups that stream faster than others take more of the tail.
+  const int32_t n_all = n_rows + 1;
+  int32_t n_static = n_all;
+  if constexpr (SRC == kSrcPaged) {
+    const int32_t pool_rows = 2 * P.splits * TILE;
+    if (P.claims != nullptr && n_all >= 8 * pool_rows) n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
+  }
   int32_t used, row_begin, row_end;
-  split_rows(n_rows + 1, P.splits, split, used, row_begin, row_end);
+  split_rows(n_static, P.splits, split, used, row_begin, row_end);
   if (split >= used) return;
   // Tiles of this split: rows row_begin + k * TILE ...; rows at or past row_end
   // belong to the next split and stay out of the sums.
@@ -831,6 +841,24 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (tile + 2 < n_tiles) load_tile(tile + 2, ba, ra);
     if (has_b) process_tile(rb);
   }
+  __shared__ int32_t s_claim;
+  if (n_static < n_all) {
+    // Pool tile c covers rows n_static + c * TILE .. (the last one ends at n_all).
+    const int32_t pool_tiles = (n_all - n_static + TILE - 1) / TILE;
+    int32_t* claim = P.claims + (int64_t)b * P.Hkv + g;
+    for (;;) {
+      if (threadIdx.x == 0) s_claim = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int32_t c = s_claim;
+      __syncthreads();  // read by every wave before the next claim overwrites it
+      if (c >= pool_tiles) break;
+      row_begin = n_static + c * TILE;
+      row_end = min(row_begin + TILE, n_all);
+      resolve_blocks(0, ba);
+      load_tile(0, ba, ra);
+      process_tile(ra);
+    }
+  }
 
   constexpr int FOLD_ROWS = kWavesPerGroup;  // rows of the LDS fold: one per wave
   __shared__ float s_wmax[kWavesPerGroup][G];
@@ -956,6 +984,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (!merges_here) return;
     __syncthreads();
     merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0]);
+    // every split has published, so none claims pool tiles any more
+    if (threadIdx.x == 0 && n_static < n_all)
+      __hip_atomic_store(P.claims + (int64_t)b * P.Hkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   // Ticket mode: every wave waits until its device-scope partial stores have
@@ -971,8 +1002,10 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   __syncthreads();
   if (!s_last) return;
   merge_and_write<DT, D, G>(P, b, g, used, false, nullptr, nullptr);
-  if (threadIdx.x == 0)  // every ticket of this launch is taken: ready for the next launch
+  if (threadIdx.x == 0) {  // every ticket (and pool tile) of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n_static < n_all) __hip_atomic_store(P.claims + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ----------------------------------------------------------------------------
