@@ -846,17 +846,38 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // Pool tile c covers rows n_static + c * TILE .. (the last one ends at n_all).
     const int32_t pool_tiles = (n_all - n_static + TILE - 1) / TILE;
     int32_t* claim = P.claims + (int64_t)b * P.Hkv + g;
-    for (;;) {
+    // Thread 0 takes the next tile index; every wave reads it after a barrier.
+    auto take = [&]() {
       if (threadIdx.x == 0) s_claim = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       const int32_t c = s_claim;
       __syncthreads();  // read by every wave before the next claim overwrites it
-      if (c >= pool_tiles) break;
+      return c;
+    };
+    auto select = [&](int32_t c) {
       row_begin = n_static + c * TILE;
       row_end = min(row_begin + TILE, n_all);
+    };
+    // One tile ahead: while tile c's K/V loads are in flight the next index is
+    // taken, and its block ids are looked up while tile c is reduced.
+    int32_t c = take();
+    if (c < pool_tiles) {
+      select(c);
       resolve_blocks(0, ba);
-      load_tile(0, ba, ra);
-      process_tile(ra);
+      for (;;) {
+        load_tile(0, ba, ra);
+        const int32_t next = take();
+        if (next < pool_tiles) {
+          select(next);
+          resolve_blocks(0, bb);
+          select(c);  // the rows of the tile being reduced
+        }
+        process_tile(ra);
+        if (next >= pool_tiles) break;
+        c = next;
+        select(c);
+        ba = bb;
+      }
     }
   }
 
