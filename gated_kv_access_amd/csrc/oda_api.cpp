@@ -255,10 +255,13 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.part_o = reinterpret_cast<float*>(c.base + c.ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(c.base + c.ws.part_ml_off);
   a.tickets = reinterpret_cast<int32_t*>(c.base + c.ws.ticket_off);
-  a.claims = reinterpret_cast<int32_t*>(c.base + c.ws.claim_off);
   // Polling needs every workgroup of the launch resident at once (the merging
-  // workgroup waits for the others): one per compute unit at most.
-  a.merge_mode = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits ? oda::kMergePoll : oda::kMergeTicket;
+  // workgroup waits for the others): one per compute unit at most.  Such a
+  // launch also balances its tail through the pool of tail tiles; larger ones
+  // already balance through the dispatch of later workgroups.
+  const bool one_round = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits;
+  a.merge_mode = one_round ? oda::kMergePoll : oda::kMergeTicket;
+  a.claims = one_round ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
