@@ -290,6 +290,20 @@ def test_ticket_and_polling_merges_share_one_workspace(full_splits, local_splits
     assert _empty_words(st) == at_init
 
 
+def test_full_pass_tail_pool_matches_oracle():
+    """With 2 Full splits per (request, KV head) the Full passes of contexts of
+    4096 rows and more keep a pool of 4 tail tiles that the splits take one at
+    a time (at the 128K workload the pool is 64 tiles of 32 splits).  Request 0
+    stays below the threshold (static splits only), 1 and 2 use the pool, the
+    last one with a ragged final pool tile.  Results match the oracle at every
+    step; every launch reuses the claim counters, so a counter its merge did
+    not reset would drop pool tiles from the next launch's result."""
+    wl = _small("tail_pool", prefill=(3000, 4500, 6151), steps=5, seed=172)
+    dims = make_dims(wl, full_splits=2)
+    st, got, want = _check_run(wl, dims=dims)
+    assert int(got.call_count.sum()) > 0, "some steps must fire"
+
+
 def test_standalone_local_and_gated_full_calls():
     wl = _small("standalone", prefill=(0, 1200, 2600), steps=1, seed=151)
     st = DecodeState(wl, gen_device="cpu")
