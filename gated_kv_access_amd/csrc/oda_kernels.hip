@@ -516,6 +516,28 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   constexpr int TILE = Gm::TILE;
   constexpr int ES = Gm::ES, QES = Gm::QES;
 
+  // Paged Full passes with the tail pool, no focus region: when the context
+  // fills the block table to within the pool and the workgroup's request
+  // turns out to be request blockIdx.z (batch 1, or every request firing), the
+  // static share of every split is fixed by the table's capacity alone, so the
+  // block ids of this split's first tile are read here, in the same round trip
+  // as the request's state.
+  int32_t spec_blk[NP];
+  int32_t spec_S = 0;
+  if constexpr (SRC == kSrcPaged) {
+    const int32_t pool_rows = 2 * P.splits * TILE;
+    const int32_t S = ((P.capacity - pool_rows) / P.splits) & ~(kSplitRowUnit - 1);
+    if (!P.rows.focus && P.claims != nullptr && S >= TILE && P.capacity >= 8 * pool_rows) {
+      spec_S = S;
+      const int32_t* bt = P.block_table + (int64_t)blockIdx.z * P.max_blocks;
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int rr = (int)(threadIdx.x & (kWave - 1)) / LPR;
+#pragma unroll
+      for (int i = 0; i < NP; ++i)  // rows < P.splits * S < capacity: inside the table row
+        spec_blk[i] = bt[((int32_t)blockIdx.x * S + (i * kWavesPerGroup + w) * RPP + rr) >> P.block_shift];
+    }
+  }
+
   // The request this workgroup serves and its committed length (-1 = none).
   int32_t b;
   int32_t committed = -1;
@@ -567,13 +589,21 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   // so workgroups that stream faster than others take more of the tail.
   const int32_t n_all = n_rows + 1;
   int32_t n_static = n_all;
-  if constexpr (SRC == kSrcPaged) {
-    const int32_t pool_rows = 2 * P.splits * TILE;
-    if (P.claims != nullptr && n_all >= 8 * pool_rows) n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
-  }
   int32_t used, row_begin, row_end;
-  split_rows(n_static, P.splits, split, used, row_begin, row_end);
-  if (split >= used) return;
+  const bool spec_hit = spec_S > 0 && b == (int32_t)blockIdx.z && n_all > P.splits * spec_S + TILE;
+  if (spec_hit) {  // the same for every workgroup of this (request, KV head)
+    n_static = P.splits * spec_S;
+    used = P.splits;
+    row_begin = split * spec_S;
+    row_end = row_begin + spec_S;
+  } else {
+    if constexpr (SRC == kSrcPaged) {
+      const int32_t pool_rows = 2 * P.splits * TILE;
+      if (P.claims != nullptr && n_all >= 8 * pool_rows) n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
+    }
+    split_rows(n_static, P.splits, split, used, row_begin, row_end);
+    if (split >= used) return;
+  }
   // Tiles of this split: rows row_begin + k * TILE ...; rows at or past row_end
   // belong to the next split and stay out of the sums.
   const int32_t n_tiles = (row_end - row_begin + TILE - 1) / TILE;
@@ -823,7 +853,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 
   TileRegs ra, rb;
   BlockIds ba, bb;
-  resolve_blocks(0, ba);
+  if (spec_hit) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) ba.blk[i] = spec_blk[i];
+  } else {
+    resolve_blocks(0, ba);
+  }
   resolve_blocks(1, bb);
   load_tile(0, ba, ra);
   if constexpr (SRC == kSrcRing) {
