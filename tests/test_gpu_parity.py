@@ -290,6 +290,22 @@ def test_ticket_and_polling_merges_share_one_workspace(full_splits, local_splits
     assert _empty_words(st) == at_init
 
 
+def test_polling_merge_over_several_rounds_of_partials():
+    """The merging split reads the partial slots in rounds of 32; with one
+    request and 2 KV heads, 64 ring splits (63 partials besides its own: two
+    rounds) and 100 Full splits (four rounds) still fit the chip at once, so
+    both merge by polling.  Outputs match the oracle and the slots read empty
+    again afterwards."""
+    wl = _small("poll_rounds", batch=1, prefill=(5000,), window=1024, steps=4, seed=173)
+    dims = make_dims(wl, full_splits=100, local_splits=64)
+    slots = wl.batch * wl.num_q_heads * 100 * (wl.head_dim + 2 * (wl.head_dim // 64))
+    st = DecodeState(wl, gen_device="cpu", dims=dims)
+    at_init = _empty_words(st)
+    assert slots <= at_init < slots + 128
+    st, got, want = _check_run(wl, dims=dims)
+    assert _empty_words(st) == at_init
+
+
 def test_full_pass_tail_pool_matches_oracle():
     """With 2 Full splits per (request, KV head) the Full passes of contexts of
     4096 rows and more keep a pool of 4 tail tiles that the splits take one at
