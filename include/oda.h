@@ -140,12 +140,12 @@ typedef struct {
 size_t oda_workspace_size(const oda_dims* dims, int32_t batch);
 
 /* Prepares the workspace (small kernels; call once after allocating it): zeroes
- * the error word and the ticket words, and marks every split-partial slot
- * empty.  Between launches the tickets read zero and the slots read empty:
- * each launch's merging workgroup finds the other splits' partials by a ticket
- * (any launch size) or by re-reading slots until none is empty (launches
- * whose workgroups are all resident at once), and leaves both as it found
- * them. */
+ * the error word, the ticket words and the tail-tile counters, and marks every
+ * split-partial slot empty.  Between launches the tickets and counters read
+ * zero and the slots read empty: each launch's merging workgroup finds the
+ * other splits' partials by a ticket (any launch size) or by re-reading slots
+ * until none is empty (launches whose workgroups are all resident at once),
+ * and leaves all of them as it found them. */
 oda_status oda_workspace_init(const oda_dims* dims, int32_t batch, void* workspace,
                               size_t workspace_bytes, oda_stream stream);
 
