@@ -582,7 +582,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     n_rows = iv.total;
   }
   // Row n_rows is the current token t, read from k_cur / v_cur: it is
-  // processed like any other row, by the last split.
+  // processed like any other row, by the last split (or, with the pool, by the
+  // workgroup that takes the last pool tile).
   // Paged passes over long ranges keep a pool of tail tiles, 2 per split, at
   // the end of the range: the splits divide rows [0, n_static) statically and
   // then take pool tiles one at a time from a per-(request, KV head) counter,
