@@ -15,9 +15,13 @@
 // across the lanes of a row with DPP and kept in the log2 domain against a
 // per-lane reference maximum; the current token (position t, which the caches
 // do not hold yet) is one more row, read from k_cur / v_cur by the last split.
-// Each workgroup leaves one (o, m, l) partial per query head, and the last
-// workgroup of each (request, KV head) to finish -- found with a ticket counter
-// in the workspace -- merges the partials into the output.
+// Ring (Local) passes use a wider geometry: one 16-byte chunk per lane and row.
+// Long paged passes end with a pool of tiles that the splits of a (request,
+// KV head) take one at a time.  Each workgroup leaves one (o, m, l) partial per
+// query head, and one workgroup of each (request, KV head) merges them into the
+// output: in a launch that fits the chip at once, the highest split, reading
+// the other partial slots until none is empty; otherwise the last workgroup to
+// take a ticket from a counter in the workspace.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -55,16 +59,6 @@ __device__ __forceinline__ float sum_over(float v) {
   } else {
     v += xor_lane<FIRST>(v);
     return sum_over<FIRST * 2, LAST>(v);
-  }
-}
-
-template <int FIRST, int LAST>
-__device__ __forceinline__ float max_over(float v) {
-  if constexpr (FIRST > LAST) {
-    return v;
-  } else {
-    v = fmaxf(v, xor_lane<FIRST>(v));
-    return max_over<FIRST * 2, LAST>(v);
   }
 }
 
@@ -108,6 +102,20 @@ __device__ __forceinline__ float row_group_max(float v) {
   if constexpr (STEP <= 2) v = fmaxf(v, row_ror<2>(v));
   if constexpr (STEP <= 1) v = fmaxf(v, row_ror<1>(v));
   return v;
+}
+
+// Max / sum over the 64 lanes of a wave, in every lane: DPP inside each
+// 16-lane row, then the four row results read as scalars (no LDS-crossbar
+// exchange on the way).
+__device__ __forceinline__ float wave_max(float v) {
+  const int r = __float_as_int(row_group_max<1>(v));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(r, 0)), __int_as_float(__builtin_amdgcn_readlane(r, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(r, 32)), __int_as_float(__builtin_amdgcn_readlane(r, 48))));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  const int r = __float_as_int(row_group_sum<1>(v));
+  return (__int_as_float(__builtin_amdgcn_readlane(r, 0)) + __int_as_float(__builtin_amdgcn_readlane(r, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(r, 32)) + __int_as_float(__builtin_amdgcn_readlane(r, 48)));
 }
 
 // Sums V values over the four 16-lane rows of a wave and spreads the V sums
@@ -477,14 +485,15 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
       for (int32_t i = lane; i < n * (kWave / 4); i += kWave) ro[(i / (kWave / 4)) * (D / 4) + i % (kWave / 4)] = e4;
       if (lane < n) *reinterpret_cast<float2*>(ml + 2 * kCopies * (base + lane)) = make_float2(empty, empty);
     }
-    const float m_new = fmaxf(M, max_over<1, 32>(mi));
+    const float m_new = fmaxf(M, wave_max(mi));
     const float keep = M == -INFINITY ? 0.f : fast_exp2(M - m_new);
     const float wi = mi == -INFINITY ? 0.f : fast_exp2(mi - m_new);
-    L = fmaf(L, keep, sum_over<1, 32>(wi * li));
-    acc *= keep;
+    L = fmaf(L, keep, wave_sum(wi * li));
+    float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i)  // lanes >= n hold weight 0
-      acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], acc);
+      part[i & 3] = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), i)), x[i], part[i & 3]);
+    acc = fmaf(acc, keep, (part[0] + part[1]) + (part[2] + part[3]));
     M = m_new;
   }
   if (own_o != nullptr) {
@@ -958,9 +967,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 
   {
     // Epilogue (one barrier): each wave rescales its row groups onto the
-    // wave's maximum per head, adds them (DPP inside 16-lane rows, row swaps
-    // across them) and stores one LDS row with its (m, l); the fold weighs the
-    // 8 wave rows by 2^(m_w - M).
+    // wave's maximum per head, adds them (row swaps across the 16-lane rows,
+    // then DPP inside them) and stores one LDS row with its (m, l); the fold
+    // weighs the 8 wave rows by 2^(m_w - M).
     constexpr int V = G * EPL;
     float v[V];
 #pragma unroll
@@ -974,9 +983,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       {
 #pragma clang fp contract(off)  // keep the scaling separate so each DPP move folds into an add
         l_acc[h] = row_group_sum<LPR>(l_acc[h] * sc);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) v[h * EPL + e] = row_group_sum<LPR>(o[h][e] * sc);
       }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[h * EPL + e] = o[h][e] * sc;
       const int li = __float_as_int(l_acc[h]);
       const float lw = (__int_as_float(__builtin_amdgcn_readlane(li, 0)) + __int_as_float(__builtin_amdgcn_readlane(li, 16))) +
                        (__int_as_float(__builtin_amdgcn_readlane(li, 32)) + __int_as_float(__builtin_amdgcn_readlane(li, 48)));
@@ -985,8 +994,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
         s_l[wave][h] = lw;
       }
     }
+    // The row swaps first (they leave a quarter of the values per lane), then
+    // the row-group sums inside each 16-lane row on what is left.
     float u[V / 4];
     wave_rows_sum_spread<V>(v, u);
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) u[k] = row_group_sum<LPR>(u[k]);
     // Lane quarter q holds values q*V/4 .. of its column (value h*EPL + e is
     // element (e / EPV * LPR + col) * EPV + e % EPV of head h): runs of RUN
     // elements, contiguous in the output row.  With LPR < 16 the lanes of a
@@ -1016,24 +1029,26 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       float Mh = s_wmax[0][h];
 #pragma unroll
       for (int w = 1; w < kWavesPerGroup; ++w) Mh = fmaxf(Mh, s_wmax[w][h]);
-      float acc = 0.f;
+      float acc = 0.f, lsum = 0.f;  // every thread also adds its rows' l
 #pragma unroll
       for (int r = 0; r < FOLD_ROWS / TPO; ++r) {
         const int row = part * (FOLD_ROWS / TPO) + r;
         const float mw = s_wmax[row][h];
-        acc = fmaf(mw == -INFINITY ? 0.f : fast_exp2(mw - Mh), s_o[row][out_i], acc);
+        const float wgt = mw == -INFINITY ? 0.f : fast_exp2(mw - Mh);
+        acc = fmaf(wgt, s_o[row][out_i], acc);
+        lsum = fmaf(wgt, s_l[row][h], lsum);
       }
-      if constexpr (TPO >= 2) acc += xor_lane<1>(acc);
-      if constexpr (TPO >= 4) acc += xor_lane<2>(acc);
+      if constexpr (TPO >= 2) {
+        acc += xor_lane<1>(acc);
+        lsum += xor_lane<1>(lsum);
+      }
+      if constexpr (TPO >= 4) {
+        acc += xor_lane<2>(acc);
+        lsum += xor_lane<2>(lsum);
+      }
       if (part != 0) continue;
       emit_o(h, e, acc);
-      if (e == 0) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w)
-          lsum = fmaf(s_wmax[w][h] == -INFINITY ? 0.f : fast_exp2(s_wmax[w][h] - Mh), s_l[w][h], lsum);
-        emit_ml(h, Mh, lsum);
-      }
+      if (e == 0) emit_ml(h, Mh, lsum);
     }
   }
 
