@@ -153,6 +153,10 @@ __device__ __forceinline__ void publish(float* p, float v) {
 __device__ __forceinline__ float collect(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A word every lane reads, loaded through the vector memory path.
+__device__ __forceinline__ int32_t vector_load(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ----------------------------------------------------------------------------
 // element formats
@@ -505,7 +509,7 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
     acc = fmaf(acc, keep, wo * own_o[tid]);
     M = m_new;
   }
-  P.out[(head0 + h) * D + e] = acc / L * P.v_scale;
+  P.out[(head0 + h) * D + e] = acc * (__builtin_amdgcn_rcpf(L) * P.v_scale);
   if (P.lse != nullptr && e == 0) P.lse[head0 + h] = (M + __log2f(L)) * kLn2;
   return true;
 }
@@ -554,9 +558,21 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) write_call_list(P);
     b = ballot_request(P, blockIdx.z, committed);
   } else if (P.gate_mode == kGateList) {
-    const bool in_list = (int32_t)blockIdx.z < *P.call_count;
-    b = in_list ? P.call_list[blockIdx.z] : -1;
-    committed = in_list ? P.call_len[blockIdx.z] : -1;  // written with the list by the gate
+    // The count and this slot's entries (written with the list by the gate)
+    // are read in one round trip: every slot below the launch's batch exists,
+    // and entries past the count are not used.  Vector loads: a scalar load
+    // here would be waited on together with the kernel-argument loads issued
+    // after it, which puts a second round trip in front of the list entries.
+    const int32_t count_v = vector_load(P.call_count);
+    const int32_t listed_v = vector_load(P.call_list + blockIdx.z);
+    const int32_t len_v = vector_load(P.call_len + blockIdx.z);
+    __builtin_amdgcn_sched_barrier(0);  // all three loads leave before the first wait
+    const int32_t count = __builtin_amdgcn_readfirstlane(count_v);
+    const int32_t listed = __builtin_amdgcn_readfirstlane(listed_v);
+    const int32_t len = __builtin_amdgcn_readfirstlane(len_v);
+    const bool in_list = (int32_t)blockIdx.z < count;
+    b = in_list ? listed : -1;
+    committed = in_list ? len : -1;
   } else {
     b = blockIdx.z;
   }
