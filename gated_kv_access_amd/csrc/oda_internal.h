@@ -77,10 +77,10 @@ struct AttnParams {
   const void* v_base;
   const int32_t* block_table;
   const int32_t* seq_len;
-  const int64_t* focus_range;
   const int32_t* call_list;   // kGateList
   const int32_t* call_count;
   const int32_t* call_len;    // kGateList: committed length of each listed request
+  const int64_t* focus_range;
   const float* score;         // kGateBallot
   float theta;
   int32_t* call_list_out;     // kGateBallot: optional outputs

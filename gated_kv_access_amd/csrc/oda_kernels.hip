@@ -153,10 +153,6 @@ __device__ __forceinline__ void publish(float* p, float v) {
 __device__ __forceinline__ float collect(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// A word every lane reads, loaded through the vector memory path.
-__device__ __forceinline__ int32_t vector_load(const int32_t* p) {
-  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ----------------------------------------------------------------------------
 // element formats
@@ -560,16 +556,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   } else if (P.gate_mode == kGateList) {
     // The count and this slot's entries (written with the list by the gate)
     // are read in one round trip: every slot below the launch's batch exists,
-    // and entries past the count are not used.  Vector loads: a scalar load
-    // here would be waited on together with the kernel-argument loads issued
-    // after it, which puts a second round trip in front of the list entries.
-    const int32_t count_v = vector_load(P.call_count);
-    const int32_t listed_v = vector_load(P.call_list + blockIdx.z);
-    const int32_t len_v = vector_load(P.call_len + blockIdx.z);
+    // and entries past the count are not used.  (The three pointers sit in one
+    // 64-byte block of the kernel arguments, loaded with the first batch.)
+    const int32_t count = *P.call_count;
+    const int32_t listed = P.call_list[blockIdx.z];
+    const int32_t len = P.call_len[blockIdx.z];
     __builtin_amdgcn_sched_barrier(0);  // all three loads leave before the first wait
-    const int32_t count = __builtin_amdgcn_readfirstlane(count_v);
-    const int32_t listed = __builtin_amdgcn_readfirstlane(listed_v);
-    const int32_t len = __builtin_amdgcn_readfirstlane(len_v);
     const bool in_list = (int32_t)blockIdx.z < count;
     b = in_list ? listed : -1;
     committed = in_list ? len : -1;
