@@ -188,21 +188,25 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 // rows.  Ring passes take one 128-row tile per workgroup and are bound by
 // latency: there a lane holds a single vector of each row (a bf16 d-128 row
 // spans a whole 16-lane DPP row) over several passes, which keeps the lane's
-// accumulators, and so the fold at the end of the pass, small.
-template <int DT, int D, int SRC = kSrcPaged>
+// accumulators, and so the fold at the end of the pass, small.  Paged passes
+// of GQA groups of 4 or more take half the vectors per lane and twice the
+// passes (the same tile), so G accumulators of a lane's elements still fit
+// two waves per SIMD without spilling.
+template <int DT, int D, int SRC = kSrcPaged, int G = 1>
 struct Geo {
   static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
   static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
   static constexpr int ROW_BYTES = D * ES;
   static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16;
-  static constexpr int NV = WIDE ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 4);  // 16-byte K/V vectors per lane per row
+  static constexpr int NARROW = !WIDE && G >= 4 ? 2 : 1;  // halves NV, doubles NP
+  static constexpr int NV = WIDE ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
   static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
   static constexpr int RPP = kWave / LPR;            // rows per wave pass
   static constexpr int EPV = 16 / ES;                // elements per 16-byte K/V vector
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1);  // passes per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * NARROW;  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
   static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
@@ -519,7 +523,8 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
 // in flight across the joins.
 template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
-  using Gm = Geo<DT, D, SRC>;
+  using Gm = Geo<DT, D, SRC, G>;
+  static_assert(Gm::TILE == Geo<DT, D, SRC>::TILE, "tile rows do not depend on the group size");
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
   constexpr int TILE = Gm::TILE;

@@ -110,6 +110,10 @@ EDGE = [
     _small("ring_exactly_one_tile", sink=4, window=124, prefill=(120, 127, 128), steps=6, seed=165),
     _small("one_request_f32_d64", dtype="f32", head_dim=64, num_q_heads=1, num_kv_heads=1, batch=1,
            prefill=(2049,), steps=4, seed=166),
+    # GQA groups of 4 stream paged rows with half the vectors per lane (the
+    # other two head sizes / types of that geometry are in SMALL and FP8)
+    _small("bf16_d64_g4", head_dim=64, num_q_heads=8, num_kv_heads=2, seed=167),
+    _small("f32_d128_g4", dtype="f32", num_q_heads=4, num_kv_heads=1, seed=168),
 ]
 
 
@@ -306,15 +310,17 @@ def test_polling_merge_over_several_rounds_of_partials():
     assert _empty_words(st) == at_init
 
 
-def test_full_pass_tail_pool_matches_oracle():
+@pytest.mark.parametrize("group", [2, 4])
+def test_full_pass_tail_pool_matches_oracle(group):
     """With 2 Full splits per (request, KV head) the Full passes of contexts of
     4096 rows and more keep a pool of 4 tail tiles that the splits take one at
     a time (at the 128K workload the pool is 64 tiles of 32 splits).  Request 0
     stays below the threshold (static splits only), 1 and 2 use the pool, the
     last one with a ragged final pool tile.  Results match the oracle at every
     step; every launch reuses the claim counters, so a counter its merge did
-    not reset would drop pool tiles from the next launch's result."""
-    wl = _small("tail_pool", prefill=(3000, 4500, 6151), steps=5, seed=172)
+    not reset would drop pool tiles from the next launch's result.  Group 4
+    runs the paged geometry with half the vectors per lane."""
+    wl = _small(f"tail_pool_g{group}", num_q_heads=2 * group, prefill=(3000, 4500, 6151), steps=5, seed=172)
     dims = make_dims(wl, full_splits=2)
     st, got, want = _check_run(wl, dims=dims)
     assert int(got.call_count.sum()) > 0, "some steps must fire"
