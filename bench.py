@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--focus", type=int, default=None, choices=(0, 1),
                     help="workload 4: a fired gated layer reads the focus set (1, default) or all positions (0)")
     ap.add_argument("--rho", type=float, default=None, help="override the Full-call rate")
+    ap.add_argument("--q-heads", type=int, default=None,
+                    help="override the query heads (a multiple of the KV heads: GQA group 1, 2 or 4)")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache storage: bf16, or FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--host-kv", action="store_true",
@@ -141,6 +143,8 @@ def build_workload(args):
         base = base.fp8()
     if args.rho is not None:
         base = base.with_(rho=(args.rho,))
+    if args.q_heads is not None:
+        base = base.with_(name=f"{base.name}_q{args.q_heads}", num_q_heads=args.q_heads)
     K = args.steps if args.steps is not None else (1024 if args.config == 2 else base.steps)
     return base, K
 
