@@ -376,8 +376,12 @@ __device__ __forceinline__ int32_t ballot_request(const AttnParams& P, int32_t s
   int32_t seen = 0;
   for (int32_t c = 0; c < P.batch; c += kWave) {
     const int32_t b = c + lane;
-    const int32_t len = b < P.batch ? P.seq_len[b] : -1;
-    const bool fire = len >= 0 && P.score[b] > P.theta;  // NaN never fires
+    const int32_t r = b < P.batch ? b : P.batch - 1;  // both words in one round trip
+    const int32_t stored = P.seq_len[r];
+    const float score = P.score[r];
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t len = b < P.batch ? stored : -1;
+    const bool fire = len >= 0 && score > P.theta;  // NaN never fires
     const uint64_t mask = __ballot(fire);
     const int32_t n = __popcll(mask);
     if (slot < seen + n) {
@@ -399,7 +403,11 @@ __device__ void write_call_list(const AttnParams& P) {
   int32_t seen = 0;
   for (int32_t c = 0; c < P.batch; c += kWave) {
     const int32_t b = c + lane;
-    const bool fire = b < P.batch && P.seq_len[b] >= 0 && P.score[b] > P.theta;
+    const int32_t r = b < P.batch ? b : P.batch - 1;  // both words in one round trip
+    const int32_t len = P.seq_len[r];
+    const float score = P.score[r];
+    __builtin_amdgcn_sched_barrier(0);
+    const bool fire = b < P.batch && len >= 0 && score > P.theta;
     const uint64_t mask = __ballot(fire);
     const uint64_t below = mask & ((1ull << lane) - 1ull);
     if (fire && P.call_list_out) P.call_list_out[seen + __popcll(below)] = b;
