@@ -20,8 +20,8 @@ namespace {
 
 constexpr int32_t kComputeUnits = 256;        // MI355X: one 8-wave workgroup fills a CU
 constexpr int32_t kFullRowsPerSplit = 16384;  // beyond this, more rounds of workgroups
-constexpr int32_t kMaxSplits = 512;
-constexpr int32_t kSplitRowUnit = 16;         // split ranges are whole units of this many rows (kernel side too)           // bounds the workspace's partials per (request, head)
+constexpr int32_t kMaxSplits = 512;           // bounds the workspace's partials per (request, head)
+constexpr int32_t kSplitRowUnit = 16;         // split ranges are whole units of this many rows (kernel side too)
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
