@@ -258,10 +258,12 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   // Polling needs every workgroup of the launch resident at once (the merging
   // workgroup waits for the others): one per compute unit at most.  Such a
   // launch also balances its tail through the pool of tail tiles; larger ones
-  // already balance through the dispatch of later workgroups.
+  // already balance through the dispatch of later workgroups.  FP8 passes keep
+  // static splits: the pool measured 3% slower for them at 128K (and no faster
+  // at 96K or 160K), where it gains 3% for bf16.
   const bool one_round = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits;
   a.merge_mode = one_round ? oda::kMergePoll : oda::kMergeTicket;
-  a.claims = one_round ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
+  a.claims = one_round && p.dtype != ODA_FP8_E4M3 ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
