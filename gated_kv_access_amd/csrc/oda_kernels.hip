@@ -353,16 +353,18 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
 // Rows [0, n) of a pass go to `splits` contiguous ranges made of whole units of
 // kSplitRowUnit rows, as even as whole units allow (range sizes differ by one
 // unit at most, so no workgroup of a launch carries a whole tile more than
-// another).  The first `used` ranges are non-empty; `split` < `used` gets
-// [begin, end).
+// another).  The larger ranges come first: the last split, which is
+// dispatched last and merges, takes the fewest rows.  The first `used` ranges
+// are non-empty; `split` < `used` gets [begin, end).
 constexpr int32_t kSplitRowUnit = 16;
 __device__ __forceinline__ void split_rows(int32_t n, int32_t splits, int32_t split, int32_t& used,
                                            int32_t& begin, int32_t& end) {
   const int32_t units = (n + kSplitRowUnit - 1) / kSplitRowUnit;
   used = units < splits ? units : splits;
   if (used < 1) used = 1;
-  begin = (int32_t)((int64_t)split * units / used) * kSplitRowUnit;
-  end = split + 1 >= used ? n : (int32_t)((int64_t)(split + 1) * units / used) * kSplitRowUnit;
+  const int32_t base = units / used, rem = units % used;
+  begin = (split * base + min(split, rem)) * kSplitRowUnit;
+  end = split + 1 >= used ? n : ((split + 1) * base + min(split + 1, rem)) * kSplitRowUnit;
 }
 
 // ----------------------------------------------------------------------------
