@@ -248,7 +248,7 @@ def main() -> int:
     if head is not None:
         extra["recall_head"] = recall_head_leg(head, head_x, wl.batch)
     if args.sweep:
-        extra = sweep(st, wl, q, k_new, v_new, K, Wm, start_len)
+        extra.update(sweep(st, wl, q, k_new, v_new, K, Wm, start_len))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,18 +377,20 @@ def roofline_leg(args, st, wl, q, k_new, v_new):
     torch.cuda.synchronize()
     avg_us = e0.elapsed_time(e1) * 1e3 / R
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    kernel = f"attention_kernel<{args.kv_dtype},{d},G{wl.num_q_heads // Hkv},paged,ballot>"
+    # The committed counters hold for the profiled kernel and workload only: the
+    # same kernel source, build variant and 128K workload, history in HBM.
     traffic = None
     tf = TRAFFIC_FILE[args.kv_dtype]
-    if args.config == 2 and os.path.exists(tf):
+    if args.config == 2 and not args.host_kv and os.path.exists(tf):
         with open(tf) as fh:
             tr = json.load(fh)
-        if tr.get("kernel_sha") == kernel_sha():
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("kernel") == kernel:
             traffic = tr.get("hbm_bytes_per_launch")
     log(f"roofline: Full-pass kernel {avg_us:.1f} us/launch, {achieved:.0f} GB/s = "
         f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak")
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": f"attention_kernel<{args.kv_dtype},{d},G{wl.num_q_heads // Hkv},paged,ballot>",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
             "avg_launch_us": round(avg_us, 2), "bytes_per_launch": bytes_per_launch, "launches": R}
 
 
