@@ -143,6 +143,18 @@ def test_ctx128k_rho0125_fp8_kv_sampled():
     _check(*out, (0, 27), (0,))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_ctx128k_gqa_group4_sampled(kv):
+    """The 128K workload with 32 query heads over the 8 KV heads (GQA group 4:
+    the paged passes' two-chunk geometry, the tail pool for bf16)."""
+    wl = W.config(2).with_(num_q_heads=32, rho=(0.5,))
+    if kv == "fp8":
+        wl = wl.fp8()
+    steps = 6
+    out = _run_and_sample(wl, steps, {0, 3, steps - 1}, (0, 27), (0,))
+    _check(*out, (0, 27), (0,))
+
+
 def test_hybrid_focus_fp8_kv_sampled():
     wl = W.config(4).fp8()
     steps = 8
