@@ -108,10 +108,11 @@ def test_decode_calls_reject_bad_arguments(lib):
     assert call(0, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, ws, None) == -4
     # misaligned query
     assert call(0, 1, FAKE + 2, FAKE, FAKE, FAKE, None, FAKE, ws, None) == -1
-    # unsupported head dim / group
-    d2 = _dims(head_dim=96)
-    assert lib.oda_decode_local(ctypes.byref(d2), ctypes.byref(kv), 0, 1, FAKE, FAKE, FAKE, FAKE, None,
-                                FAKE, 1 << 30, None) == -2
+    # unsupported head dim / group (groups 1, 2 and 4 are built)
+    for d2 in (_dims(head_dim=96), _dims(num_q_heads=16, num_kv_heads=2), _dims(num_q_heads=6, num_kv_heads=2)):
+        assert lib.oda_decode_local(ctypes.byref(d2), ctypes.byref(kv), 0, 1, FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, 1 << 30, None) == -2
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=8, num_kv_heads=2)), 1) > 0
     # missing ring
     kv2 = _kv()
     kv2.k_ring = None
