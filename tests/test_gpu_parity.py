@@ -354,6 +354,59 @@ def test_standalone_local_and_gated_full_calls():
                              f"standalone layer {layer}")
 
 
+def test_device_errors_skip_and_flag_without_touching_other_requests():
+    """Inputs that only the device can see are caught by the kernels' own
+    checks: a block id outside the cache skips the rows it would address, a
+    context longer than the block table skips the request; each sets its bit in
+    the workspace's error word, and the other requests' outputs still match the
+    oracle."""
+    wl = _small("deverr", prefill=(300, 1200, 2600), steps=1, seed=181)
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")[0].cuda()
+    k_new, v_new = st.decode_inputs()
+    score = torch.ones(wl.batch, dtype=torch.float32, device="cuda")  # every request fires
+    ks, vs = oracle_sequences(st)
+    want = orc.decode_run(oracle_cfg(wl), wl.prefill, ks, vs, words(q.unsqueeze(0)),
+                          score.cpu().numpy()[None, :])["out"][0, 0]
+    args = (q[0].contiguous(), k_new[0, 0].contiguous(), v_new[0, 0].contiguous())
+
+    def full_pass():
+        out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), 7.0, device="cuda")
+        B.decode_full_gated(st.dims, st.kv, 0, wl.batch, *args, score, 0.0, out, None, None, None, st.workspace)
+        torch.cuda.synchronize()
+        err = st.device_error()
+        st.workspace[:4].zero_()
+        return out.cpu().numpy(), err
+
+    out, err = full_pass()
+    assert err == 0
+    assert_outputs_close(out[None, None], want[None, None], wl.dtype, "clean")
+    # a physical block id past the cache in request 1's table row
+    saved = int(st.block_table[1, 10].item())
+    st.block_table[1, 10] = st.num_blocks + 7
+    out, err = full_pass()
+    st.block_table[1, 10] = saved
+    say(f"bad block id: error word {err}")
+    assert err == B.DEVERR_BLOCK_ID
+    assert np.isfinite(out[1]).all()
+    for b in (0, 2):
+        assert_outputs_close(out[None, None, b:b + 1], want[None, None, b:b + 1], wl.dtype, f"bad block, request {b}")
+    # a committed length past the block table's capacity for request 2
+    cap = st.dims.max_blocks_per_seq * wl.block_size
+    st.seq_len[2] = cap + 5
+    out, err = full_pass()
+    st.seq_len[2] = wl.prefill[2]
+    say(f"context beyond capacity: error word {err}")
+    assert err == B.DEVERR_CAPACITY
+    assert (out[2] == 7.0).all(), "the request is skipped: its output rows stay untouched"
+    for b in (0, 1):
+        assert_outputs_close(out[None, None, b:b + 1], want[None, None, b:b + 1], wl.dtype, f"capacity, request {b}")
+    out, err = full_pass()
+    assert err == 0
+    assert_outputs_close(out[None, None], want[None, None], wl.dtype, "clean again")
+
+
 # ---------------------------------------------------------------- FP8 E4M3 KV cache
 
 FP8 = [
