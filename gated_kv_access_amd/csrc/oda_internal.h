@@ -129,7 +129,7 @@ int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float*
                   oda_stream s);
 // Device address of pinned host memory: 0, 1 (not pinned host memory) or 2 (runtime error).
 int host_device_pointer(void* host_ptr, void** device_ptr);
-// Rows per workgroup iteration for the attention kernel built for (dtype, d, source).
-int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source);
+// Rows per workgroup iteration for the attention kernel built for (dtype, d, source, group).
+int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source, int32_t group);
 
 }  // namespace oda

@@ -189,16 +189,18 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 // latency: there a lane holds a single vector of each row (a bf16 d-128 row
 // spans a whole 16-lane DPP row) over several passes, which keeps the lane's
 // accumulators, and so the fold at the end of the pass, small.  Paged passes
-// of GQA groups of 4 or more take half the vectors per lane and twice the
-// passes (the same tile), so G accumulators of a lane's elements still fit
-// two waves per SIMD without spilling.
+// of GQA groups of 4 take half the vectors per lane and twice the passes (the
+// same tile), so G accumulators of a lane's elements still fit two waves per
+// SIMD without spilling; groups of 8 take a quarter of the vectors and twice
+// the passes, a tile half as tall.
 template <int DT, int D, int SRC = kSrcPaged, int G = 1>
 struct Geo {
   static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
   static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
   static constexpr int ROW_BYTES = D * ES;
   static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16;
-  static constexpr int NARROW = !WIDE && G >= 4 ? 2 : 1;  // halves NV, doubles NP
+  static constexpr int NARROW = WIDE ? 1 : (G >= 8 ? 4 : (G >= 4 ? 2 : 1));  // divides NV
+  static constexpr int PASSES = WIDE ? 1 : (G >= 4 ? 2 : 1);                  // multiplies NP
   static constexpr int NV = WIDE ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
   static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
   static constexpr int RPP = kWave / LPR;            // rows per wave pass
@@ -206,7 +208,7 @@ struct Geo {
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * NARROW;  // passes per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * PASSES;  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
   static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
@@ -434,7 +436,8 @@ __device__ __forceinline__ bool slot_empty(float x) { return __float_as_uint(x) 
 
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
 
-// One thread per output element (h, e); a wave serves one head.  Partials
+// One thread per output element (h, e) (two when G * d exceeds the
+// workgroup); a wave serves one head at a time.  Partials
 // 0..n_mem-1 are read from the workspace in rounds of up to kMergeBatch:
 // lane i loads (m, l) of partial i of the round (one 8-byte load), every lane
 // loads its element of each partial's o, the round's maximum and weights come
@@ -445,12 +448,8 @@ constexpr int kMergeBatch = 32;  // partials loaded per round by one output thre
 // next launch as soon as they are read.  Returns false (and sets ODA_DEVERR_MERGE_WAIT) if polling gives up.
 // No LDS writes, no barrier.
 template <int DT, int D, int G>
-__device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
-                                const float* own_o, const float* own_ml) {
-  constexpr int GD = G * D;
-  static_assert(GD <= kGroupThreads && D % kWave == 0, "one thread per output, one head per wave");
-  const int tid = threadIdx.x;
-  if (tid >= GD) return true;
+__device__ bool merge_output(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
+                             const float* own_o, const float* own_ml, int tid) {
   const int lane = tid & (kWave - 1);
   const int h = tid / D, e = tid % D;
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
@@ -524,6 +523,15 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
   return true;
 }
 
+template <int DT, int D, int G>
+__device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
+                                const float* own_o, const float* own_ml) {
+  static_assert(D % kWave == 0, "one head per wave");
+  for (int tid = threadIdx.x; tid < G * D; tid += kGroupThreads)
+    if (!merge_output<DT, D, G>(P, b, g, n_mem, poll, own_o, own_ml, tid)) return false;
+  return true;
+}
+
 // ----------------------------------------------------------------------------
 // one attention pass of one layer: split-K partials + last-workgroup merge
 
@@ -534,7 +542,6 @@ __device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32
 template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
   using Gm = Geo<DT, D, SRC, G>;
-  static_assert(Gm::TILE == Geo<DT, D, SRC>::TILE, "tile rows do not depend on the group size");
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
   constexpr int TILE = Gm::TILE;
@@ -1500,7 +1507,7 @@ int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   if (a.rows.source == kSrcRing) {
     // Splits no longer than a tile (the usual case at small batch) skip empty passes.
     const int32_t units = (a.rows.ring_slots + 1 + kSplitRowUnit - 1) / kSplitRowUnit;
-    const bool skip = (int64_t)((units + a.splits - 1) / a.splits) * kSplitRowUnit <= Geo<DT, D, kSrcRing>::TILE;
+    const bool skip = (int64_t)((units + a.splits - 1) / a.splits) * kSplitRowUnit <= Geo<DT, D, kSrcRing, G>::TILE;
     if (ballot) {
       if (skip) hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true, true>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((attention_kernel<DT, D, G, kSrcRing, true, false>), grid, block, 0, s, a);
@@ -1515,28 +1522,39 @@ int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   return (int)hipGetLastError();
 }
 
+// Groups of 8 are built where a lane's share of a row can be one 16-byte chunk
+// of at most 16 lanes and eight heads' accumulators fit: bf16, and f32 with
+// d = 64 (the host reports the others unsupported).
+template <int DT, int D>
+constexpr bool kGroup8Built = DT == ODA_BF16 || (DT == ODA_F32 && D == 64);
+
 template <int DT, int D>
 int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {
   switch (p.G) {
     case 1: return launch_attention_t<DT, D, 1>(a, batch, s);
     case 2: return launch_attention_t<DT, D, 2>(a, batch, s);
     case 4: return launch_attention_t<DT, D, 4>(a, batch, s);
+    case 8:
+      if constexpr (kGroup8Built<DT, D>) return launch_attention_t<DT, D, 8>(a, batch, s);
+      return (int)hipErrorInvalidValue;
     default: return (int)hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-template <int SRC>
+template <int SRC, int G>
 int tile_rows_src(int32_t dtype, int32_t head_dim) {
-  if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128, SRC>::TILE : Geo<ODA_BF16, 64, SRC>::TILE;
+  if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128, SRC, G>::TILE : Geo<ODA_BF16, 64, SRC, G>::TILE;
   if (dtype == ODA_FP8_E4M3)
     return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128, SRC>::TILE : Geo<ODA_FP8_E4M3, 64, SRC>::TILE;
-  return head_dim == 128 ? Geo<ODA_F32, 128, SRC>::TILE : Geo<ODA_F32, 64, SRC>::TILE;
+  return head_dim == 128 ? Geo<ODA_F32, 128, SRC, (G >= 8 ? 1 : G)>::TILE : Geo<ODA_F32, 64, SRC, G>::TILE;
 }
 
-int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source) {
-  return source == kSrcRing ? tile_rows_src<kSrcRing>(dtype, head_dim) : tile_rows_src<kSrcPaged>(dtype, head_dim);
+int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source, int32_t group) {
+  if (group >= 8)
+    return source == kSrcRing ? tile_rows_src<kSrcRing, 8>(dtype, head_dim) : tile_rows_src<kSrcPaged, 8>(dtype, head_dim);
+  return source == kSrcRing ? tile_rows_src<kSrcRing, 1>(dtype, head_dim) : tile_rows_src<kSrcPaged, 1>(dtype, head_dim);
 }
 
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {

@@ -71,7 +71,15 @@ def test_workspace_size_valid_and_invalid(lib):
     assert lib.oda_workspace_size(ctypes.byref(_dims()), 4) == 0                   # batch > max_batch
     assert lib.oda_workspace_size(ctypes.byref(_dims(reserved0=1)), 1) == 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(head_dim=96)), 1) == 0        # not built
-    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2)), 1) == 0  # group 8
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=32, num_kv_heads=2)), 1) == 0  # group 16
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=6, num_kv_heads=2)), 1) == 0   # group 3
+    # group 8: built for bf16 and for f32 with d = 64
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2)), 1) > 0
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.F32,
+                                                     head_dim=64)), 1) > 0
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.F32)), 1) == 0
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.FP8_E4M3)),
+                                  1) == 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(kv_dtype=3)), 1) == 0
     for bad in (-1.0, float("nan"), float("inf")):
         assert lib.oda_workspace_size(ctypes.byref(_dims(k_scale=bad)), 1) == 0
@@ -108,11 +116,12 @@ def test_decode_calls_reject_bad_arguments(lib):
     assert call(0, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, ws, None) == -4
     # misaligned query
     assert call(0, 1, FAKE + 2, FAKE, FAKE, FAKE, None, FAKE, ws, None) == -1
-    # unsupported head dim / group (groups 1, 2 and 4 are built)
-    for d2 in (_dims(head_dim=96), _dims(num_q_heads=16, num_kv_heads=2), _dims(num_q_heads=6, num_kv_heads=2)):
+    # unsupported head dim / group (groups 1, 2, 4 and, for bf16, 8 are built)
+    for d2 in (_dims(head_dim=96), _dims(num_q_heads=32, num_kv_heads=2), _dims(num_q_heads=6, num_kv_heads=2)):
         assert lib.oda_decode_local(ctypes.byref(d2), ctypes.byref(kv), 0, 1, FAKE, FAKE, FAKE, FAKE, None,
                                     FAKE, 1 << 30, None) == -2
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=8, num_kv_heads=2)), 1) > 0
+    assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2)), 1) > 0
     # missing ring
     kv2 = _kv()
     kv2.k_ring = None

@@ -114,6 +114,11 @@ EDGE = [
     # other two head sizes / types of that geometry are in SMALL and FP8)
     _small("bf16_d64_g4", head_dim=64, num_q_heads=8, num_kv_heads=2, seed=167),
     _small("f32_d128_g4", dtype="f32", num_q_heads=4, num_kv_heads=1, seed=168),
+    # GQA groups of 8: one chunk per lane and row, tiles half as tall; the
+    # merge serves two outputs per thread at d = 128
+    _small("bf16_d128_g8", num_q_heads=16, num_kv_heads=2, seed=169),
+    _small("bf16_d64_g8", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=170),
+    _small("f32_d64_g8", dtype="f32", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=171),
 ]
 
 
@@ -310,7 +315,7 @@ def test_polling_merge_over_several_rounds_of_partials():
     assert _empty_words(st) == at_init
 
 
-@pytest.mark.parametrize("group", [2, 4])
+@pytest.mark.parametrize("group", [2, 4, 8])
 def test_full_pass_tail_pool_matches_oracle(group):
     """With 2 Full splits per (request, KV head) the Full passes of contexts of
     4096 rows and more keep a pool of 4 tail tiles that the splits take one at
@@ -318,8 +323,9 @@ def test_full_pass_tail_pool_matches_oracle(group):
     stays below the threshold (static splits only), 1 and 2 use the pool, the
     last one with a ragged final pool tile.  Results match the oracle at every
     step; every launch reuses the claim counters, so a counter its merge did
-    not reset would drop pool tiles from the next launch's result.  Group 4
-    runs the paged geometry with half the vectors per lane."""
+    not reset would drop pool tiles from the next launch's result.  Groups 4
+    and 8 run the paged geometries with fewer vectors per lane (and, at 8, a
+    tile half as tall)."""
     wl = _small(f"tail_pool_g{group}", num_q_heads=2 * group, prefill=(3000, 4500, 6151), steps=5, seed=172)
     dims = make_dims(wl, full_splits=2)
     st, got, want = _check_run(wl, dims=dims)
