@@ -143,11 +143,12 @@ def test_ctx128k_rho0125_fp8_kv_sampled():
     _check(*out, (0, 27), (0,))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_ctx128k_gqa_group4_sampled(kv):
-    """The 128K workload with 32 query heads over the 8 KV heads (GQA group 4:
-    the paged passes' two-chunk geometry, the tail pool for bf16)."""
-    wl = W.config(2).with_(num_q_heads=32, rho=(0.5,))
+@pytest.mark.parametrize("group,kv", [(4, "bf16"), (4, "fp8"), (8, "bf16")])
+def test_ctx128k_gqa_groups_sampled(group, kv):
+    """The 128K workload with 32 or 64 query heads over the 8 KV heads (GQA
+    groups of 4 and 8: the paged passes' narrower geometries, the tail pool
+    for bf16)."""
+    wl = W.config(2).with_(num_q_heads=8 * group, rho=(0.5,))
     if kv == "fp8":
         wl = wl.fp8()
     steps = 6
