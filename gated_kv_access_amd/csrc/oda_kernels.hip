@@ -139,6 +139,21 @@ __device__ __forceinline__ void wave_rows_sum_spread(const float (&v)[V], float 
   }
 }
 
+// Max / sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one column of the four
+// 16-lane rows), left in all four: the same two row swaps.
+__device__ __forceinline__ float quarters_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quarters_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // A lane rescales its running sums only when a score exceeds its reference
 // maximum by more than this (log2 domain): weights stay below 2^8, far from
 // fp32 overflow, and the result is exact whatever the reference is.
@@ -158,6 +173,9 @@ __device__ __forceinline__ float collect(const float* p) {
 // element formats
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -192,26 +210,35 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 // of GQA groups of 4 take half the vectors per lane and twice the passes (the
 // same tile), so G accumulators of a lane's elements still fit two waves per
 // SIMD without spilling; groups of 8 take a quarter of the vectors and twice
-// the passes, a tile half as tall.
+// the passes, a tile half as tall.  Paged passes of bf16 and FP8 groups of 4
+// and 8 (MF) put both products on MFMA instead: lane l holds chunks 4j + l/16
+// of row l % 16 of each 16-row pass; each 8 of its elements (FP8 widened to
+// bf16) are the A operand of one 16x16x32 bf16 form for S^T = K Q^T, the
+// matching query elements its B operand; the scores come out as the B
+// operand of the 16x16x16 form for O^T += V^T P^T, whose A operand (V
+// transposed, as bf16) is read back from LDS.
 template <int DT, int D, int SRC = kSrcPaged, int G = 1>
 struct Geo {
   static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
   static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
   static constexpr int ROW_BYTES = D * ES;
   static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16;
-  static constexpr int NARROW = WIDE ? 1 : (G >= 8 ? 4 : (G >= 4 ? 2 : 1));  // divides NV
-  static constexpr int PASSES = WIDE ? 1 : (G >= 4 ? 2 : 1);                  // multiplies NP
-  static constexpr int NV = WIDE ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
+  static constexpr bool MF = SRC == kSrcPaged && DT != ODA_F32 && G >= 4;
+  static constexpr int NARROW = WIDE || MF ? 1 : (G >= 8 ? 4 : (G >= 4 ? 2 : 1));  // divides NV
+  static constexpr int PASSES = WIDE || MF ? 1 : (G >= 4 ? 2 : 1);                  // multiplies NP
+  static constexpr int NV = WIDE ? 1 : MF ? D * ES / 64 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
   static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
   static constexpr int RPP = kWave / LPR;            // rows per wave pass
   static constexpr int EPV = 16 / ES;                // elements per 16-byte K/V vector
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * PASSES;  // passes per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : MF ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 1) * PASSES;  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
   static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
+  static_assert(!MF || (LPR == 4 && RPP == 16 && NP == 1 && G <= 16 && QV == NV * QPV && QES == 2),
+                "MFMA pass: 16 rows of 4 lanes, one pass, bf16 queries");
 };
 
 // One element of a stored K/V row and of a query row, widened to f32.
@@ -562,7 +589,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       spec_S = S;
       const int32_t* bt = P.block_table + (int64_t)blockIdx.z * P.max_blocks;
       const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-      const int rr = (int)(threadIdx.x & (kWave - 1)) / LPR;
+      const int rr = Gm::MF ? (int)(threadIdx.x % RPP) : (int)(threadIdx.x & (kWave - 1)) / LPR;
 #pragma unroll
       for (int i = 0; i < NP; ++i)  // rows < P.splits * S < capacity: inside the table row
         spec_blk[i] = bt[((int32_t)blockIdx.x * S + (i * kWavesPerGroup + w) * RPP + rr) >> P.block_shift];
@@ -650,13 +677,24 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane % LPR;
-  const int rrow = lane / LPR;
+  // A lane's row within its wave's pass and its chunk group within the row.
+  const int sub = Gm::MF ? lane / RPP : lane % LPR;
+  const int rrow = Gm::MF ? lane % RPP : lane / LPR;
 
   // Query heads g*G .. g*G+G-1, in this lane's element slots.
   // Query vector j covers the elements of K/V vector j / QPV.
-  uint4 qv[G][QV];
-  {
+  // (MF: the B operand of S^T = K Q^T, head lane % 16, zero past the group.)
+  constexpr int QH = Gm::MF ? 1 : G;
+  uint4 qv[QH][QV];
+  if constexpr (Gm::MF) {
+    const char* qbase = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + (int64_t)g * G) * D * QES;
+    const int hq = lane % 16;
+#pragma unroll
+    for (int j = 0; j < QV; ++j)
+      qv[0][j] = hq < G ? *reinterpret_cast<const uint4*>(qbase + (int64_t)hq * D * QES +
+                                                          ((j / QPV) * LPR + sub) * EPV * QES + (j % QPV) * 16)
+                        : make_uint4(0, 0, 0, 0);
+  } else {
     const char* qbase = static_cast<const char*>(P.q) + ((int64_t)b * P.Hq + (int64_t)g * G) * D * QES;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -675,14 +713,27 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   const int32_t bmask = (1 << P.block_shift) - 1;
   const int64_t cur_off = ((int64_t)b * P.Hkv + g) * D * ES;
 
-  float m_run[G], l_acc[G], o[G][EPL];
+  constexpr int OE = Gm::MF ? 1 : EPL;
+  float m_run[G], l_acc[G], o[G][OE];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_acc[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    for (int e = 0; e < OE; ++e) o[h][e] = 0.f;
   }
+  // MF: O^T tiles (lane l: elements 16 mi + 4 (l / 16) + r of head l % 16),
+  // and the running reference and weight sum of head l % 16, the same in the
+  // four lanes of the head.  V rows are staged per wave in LDS (row stride
+  // VST bytes: the four row quarters of a transposed read fall on different
+  // banks).
+  constexpr int MT = Gm::MF ? D / 16 : 1;
+  constexpr int VST = 2 * D + 16;
+  f32x4_t acc_mf[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) acc_mf[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_mf = -INFINITY, l_mf = 0.f;
+  __shared__ __align__(16) char s_vt[Gm::MF ? kWavesPerGroup * 16 * VST : 16];
 
   // Tile registers: K and V of NP passes plus their validity.  Two sets
   // ping-pong so the loads of tile i+1 are in flight while tile i is reduced.
@@ -764,6 +815,78 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   };
 
   auto process_tile = [&](TileRegs& R) {
+    if constexpr (Gm::MF) {
+      if (SKIP && !R.live[0]) return;
+      // S^T = K Q^T: lane l gets the scores of rows 4 (l / 16) + r of head l % 16.
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < QV; ++j) {  // the lane's row elements 8j .. 8j + 7
+        uint4 ka = R.k[0][j / QPV];
+        if constexpr (DT == ODA_FP8_E4M3) {
+          const uint32_t w0 = j % 2 ? ka.z : ka.x, w1 = j % 2 ? ka.w : ka.y;
+          ka = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                          fp8x2_to_bf16x2<true>(w1));
+        }
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                     __builtin_bit_cast(bf16x8_t, qv[0][j]), sc, 0, 0, 0);
+      }
+      // The pass's V rows go to LDS as bf16 rows.
+      char* vt = s_vt + wave * 16 * VST;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        char* dst = vt + rrow * VST + (j * LPR + sub) * EPV * 2;
+        if constexpr (DT == ODA_FP8_E4M3) {
+          const uint4 w = R.v[0][j];
+          *reinterpret_cast<uint4*>(dst) = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                                      fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+          *reinterpret_cast<uint4*>(dst + 16) = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                                           fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
+        } else {
+          *reinterpret_cast<uint4*>(dst) = R.v[0][j];
+        }
+      }
+      const uint64_t vm = __ballot(R.valid[0]);  // bit r: row r of the pass is in the sums
+      const int q4 = (lane >> 4) * 4;
+      float s[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r] = (vm >> (q4 + r)) & 1 ? sc[r] * P.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = quarters_max(mx);
+      if (mx > m_mf + kRescaleGap) {
+        const float alpha = m_mf == -INFINITY ? 0.f : fast_exp2(m_mf - mx);
+        l_mf *= alpha;
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) acc_mf[mi] *= alpha;
+        m_mf = mx;
+      }
+      // P^T as a sum of two bf16 parts (the second holds what rounding the
+      // first lost), so the weights keep about 16 bits in the products.
+      i16x4_t ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float w = s[r] == -INFINITY ? 0.f : fast_exp2(s[r] - m_mf);
+        const __bf16 wh = (__bf16)w;
+        ph[r] = __builtin_bit_cast(short, wh);
+        pl[r] = __builtin_bit_cast(short, (__bf16)(w - (float)wh));
+        l_mf += w;
+      }
+      // O^T += V^T P^T, 16 elements at a time: lane l reads element
+      // 16 mi + l % 16 of rows 4 (l / 16) + r.
+      const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+      i16x4_t va[MT];
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) va[mi][r] = (short)vt16[(q4 + r) * (VST / 2) + 16 * mi + lane % 16];
+        acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], ph, acc_mf[mi], 0, 0, 0);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+        acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], pl, acc_mf[mi], 0, 0, 0);
+    } else {
     if constexpr (SRC == kSrcRing) {
       // Membership in S^L_t; rows outside it never reach the sums (slots not
       // yet written may hold anything, so their values are replaced by zeros).
@@ -889,6 +1012,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
         }
       }
     }
+    }
   };
 
   TileRegs ra, rb;
@@ -1000,6 +1124,23 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     // wave's maximum per head, adds them (row swaps across the 16-lane rows,
     // then DPP inside them) and stores one LDS row with its (m, l); the fold
     // weighs the 8 wave rows by 2^(m_w - M).
+    if constexpr (Gm::MF) {
+      // A wave's O^T tiles already sum its rows (its reference is one per
+      // head): lane l stores elements 16 mi + 4 (l / 16) .. + 3 of head l % 16;
+      // the four lanes of a head add their weight sums.
+      const float lw = quarters_sum(l_mf);
+      const int h = lane % 16;
+      if (h < G) {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+          *reinterpret_cast<float4*>(&s_o[wave][h * D + 16 * mi + (lane >> 4) * 4]) =
+              make_float4(acc_mf[mi][0], acc_mf[mi][1], acc_mf[mi][2], acc_mf[mi][3]);
+        if (lane < 16) {
+          s_wmax[wave][h] = m_mf;
+          s_l[wave][h] = lw;
+        }
+      }
+    } else {
     constexpr int V = G * EPL;
     float v[V];
 #pragma unroll
@@ -1051,6 +1192,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
           for (int k = 0; k < RUN; ++k) dst[k] = u[k0 + k];
         }
       }
+    }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D * TPO; idx += kGroupThreads) {
@@ -1522,9 +1664,10 @@ int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   return (int)hipGetLastError();
 }
 
-// Groups of 8 are built where a lane's share of a row can be one 16-byte chunk
-// of at most 16 lanes and eight heads' accumulators fit: bf16, and f32 with
-// d = 64 (the host reports the others unsupported).
+// Groups of 8 are built where the ring passes' lane share of a row can be one
+// 16-byte chunk of at most 16 lanes and eight heads' accumulators fit without
+// spilling: bf16 (its paged passes on MFMA), and f32 with d = 64 (FP8 ring
+// passes would spill; the host reports the others unsupported).
 template <int DT, int D>
 constexpr bool kGroup8Built = DT == ODA_BF16 || (DT == ODA_F32 && D == 64);
 

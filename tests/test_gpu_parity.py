@@ -114,8 +114,9 @@ EDGE = [
     # other two head sizes / types of that geometry are in SMALL and FP8)
     _small("bf16_d64_g4", head_dim=64, num_q_heads=8, num_kv_heads=2, seed=167),
     _small("f32_d128_g4", dtype="f32", num_q_heads=4, num_kv_heads=1, seed=168),
-    # GQA groups of 8: one chunk per lane and row, tiles half as tall; the
-    # merge serves two outputs per thread at d = 128
+    # GQA groups of 8: the paged passes on MFMA for bf16 (one chunk per lane
+    # and row, tiles half as tall, for f32 and in the ring passes); the merge
+    # serves two outputs per thread at d = 128
     _small("bf16_d128_g8", num_q_heads=16, num_kv_heads=2, seed=169),
     _small("bf16_d64_g8", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=170),
     _small("f32_d64_g8", dtype="f32", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=171),
