@@ -72,11 +72,11 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
     if ((int64_t)d->sink + d->window > (int64_t)1 << 24) return ODA_ERR_INVALID_ARG;
   }
   if (p->Ls > 0 && (d->sw_window < 1 || d->sw_window > (1 << 24))) return ODA_ERR_INVALID_ARG;
-  // Built variants: d in {64, 128}, group in {1, 2, 4}; group 8 for bf16, and
-  // for f32 with d = 64.
+  // Built variants: d in {64, 128}, group in {1, 2, 4}; group 8 for bf16 and
+  // FP8, and for f32 with d = 64.
   if (p->D != 64 && p->D != 128) return ODA_ERR_UNSUPPORTED;
   if (p->G != 1 && p->G != 2 && p->G != 4 && p->G != 8) return ODA_ERR_UNSUPPORTED;
-  if (p->G == 8 && !(p->dtype == ODA_BF16 || (p->dtype == ODA_F32 && p->D == 64))) return ODA_ERR_UNSUPPORTED;
+  if (p->G == 8 && p->dtype == ODA_F32 && p->D != 64) return ODA_ERR_UNSUPPORTED;
   p->ring_slots = p->Lg > 0 ? p->sink + p->window : 0;
   p->block_shift = 0;
   if (p->Lg > 0)

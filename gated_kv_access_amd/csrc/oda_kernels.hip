@@ -210,8 +210,8 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 // of GQA groups of 4 take half the vectors per lane and twice the passes (the
 // same tile), so G accumulators of a lane's elements still fit two waves per
 // SIMD without spilling; groups of 8 take a quarter of the vectors and twice
-// the passes, a tile half as tall.  Paged passes of bf16 and FP8 groups of 4
-// and 8 (MF) put both products on MFMA instead: lane l holds chunks 4j + l/16
+// the passes, a tile half as tall.  Passes of bf16 and FP8 groups of 4 and 8
+// (MF) put both products on MFMA instead: lane l holds chunks 4j + l/16
 // of row l % 16 of each 16-row pass; each 8 of its elements (FP8 widened to
 // bf16) are the A operand of one 16x16x32 bf16 form for S^T = K Q^T, the
 // matching query elements its B operand; the scores come out as the B
@@ -222,8 +222,8 @@ struct Geo {
   static constexpr int ES = DT == ODA_F32 ? 4 : (DT == ODA_BF16 ? 2 : 1);  // K/V element bytes
   static constexpr int QES = DT == ODA_F32 ? 4 : 2;                          // query element bytes
   static constexpr int ROW_BYTES = D * ES;
-  static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16;
-  static constexpr bool MF = SRC == kSrcPaged && DT != ODA_F32 && G >= 4;
+  static constexpr bool MF = DT != ODA_F32 && G >= 4;
+  static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16 && !MF;
   static constexpr int NARROW = WIDE || MF ? 1 : (G >= 8 ? 4 : (G >= 4 ? 2 : 1));  // divides NV
   static constexpr int PASSES = WIDE || MF ? 1 : (G >= 4 ? 2 : 1);                  // multiplies NP
   static constexpr int NV = WIDE ? 1 : MF ? D * ES / 64 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
@@ -817,7 +817,16 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   auto process_tile = [&](TileRegs& R) {
     if constexpr (Gm::MF) {
       if (SKIP && !R.live[0]) return;
-      // S^T = K Q^T: lane l gets the scores of rows 4 (l / 16) + r of head l % 16.
+      if constexpr (SRC == kSrcRing) {  // membership in S^L_t: other slots may hold anything
+        bool in_local = R.valid[0] && R.row[0] == n_rows;
+        if (R.valid[0] && !in_local) ring_slot_position(rst, R.row[0], in_local);
+        R.valid[0] = in_local;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          if (!in_local) R.v[0][j] = make_uint4(0, 0, 0, 0);
+      }
+      // S^T = K Q^T: lane l gets the scores of rows 4 (l / 16) + r of head l % 16
+      // (a row outside the sums may hold anything; its scores are dropped).
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QV; ++j) {  // the lane's row elements 8j .. 8j + 7
@@ -1664,12 +1673,11 @@ int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   return (int)hipGetLastError();
 }
 
-// Groups of 8 are built where the ring passes' lane share of a row can be one
-// 16-byte chunk of at most 16 lanes and eight heads' accumulators fit without
-// spilling: bf16 (its paged passes on MFMA), and f32 with d = 64 (FP8 ring
-// passes would spill; the host reports the others unsupported).
+// Groups of 8 are built for bf16 and FP8 (both products on MFMA) and for f32
+// with d = 64, whose row fits one 16-byte chunk per lane of a 16-lane row with
+// eight heads' accumulators (the host reports f32 with d = 128 unsupported).
 template <int DT, int D>
-constexpr bool kGroup8Built = DT == ODA_BF16 || (DT == ODA_F32 && D == 64);
+constexpr bool kGroup8Built = DT != ODA_F32 || D == 64;
 
 template <int DT, int D>
 int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {

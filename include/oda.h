@@ -96,7 +96,7 @@ typedef struct {
   int32_t num_q_heads;         /* Hq                                                     */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0; query head h reads KV head h/(Hq/Hkv);
                                   built for groups Hq/Hkv of 1, 2 and 4, and 8 for
-                                  bf16 and for f32 with d = 64 (else ODA_ERR_UNSUPPORTED) */
+                                  bf16, FP8 and f32 with d = 64 (else ODA_ERR_UNSUPPORTED) */
   int32_t head_dim;            /* d: 64 or 128                                           */
   int32_t sink;                /* s >= 0 of gated layers                                 */
   int32_t window;              /* w >= 1 of gated layers; gated ring has s+w slots       */

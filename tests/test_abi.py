@@ -73,13 +73,13 @@ def test_workspace_size_valid_and_invalid(lib):
     assert lib.oda_workspace_size(ctypes.byref(_dims(head_dim=96)), 1) == 0        # not built
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=32, num_kv_heads=2)), 1) == 0  # group 16
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=6, num_kv_heads=2)), 1) == 0   # group 3
-    # group 8: built for bf16 and for f32 with d = 64
+    # group 8: built for bf16, FP8 and f32 with d = 64
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2)), 1) > 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.F32,
                                                      head_dim=64)), 1) > 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.F32)), 1) == 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(num_q_heads=16, num_kv_heads=2, kv_dtype=B.FP8_E4M3)),
-                                  1) == 0
+                                  1) > 0
     assert lib.oda_workspace_size(ctypes.byref(_dims(kv_dtype=3)), 1) == 0
     for bad in (-1.0, float("nan"), float("inf")):
         assert lib.oda_workspace_size(ctypes.byref(_dims(k_scale=bad)), 1) == 0
