@@ -120,6 +120,10 @@ EDGE = [
     _small("bf16_d128_g8", num_q_heads=16, num_kv_heads=2, seed=169),
     _small("bf16_d64_g8", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=170),
     _small("f32_d64_g8", dtype="f32", head_dim=64, num_q_heads=8, num_kv_heads=1, seed=171),
+    # MFMA ring passes over a ring that wraps many times (slots of older
+    # positions inside a pass), and a short request that never fills it
+    _small("ring_wrap_g8", num_q_heads=16, num_kv_heads=2, sink=2, window=16, prefill=(100, 37, 5),
+           steps=40, block_size=64, seed=172),
 ]
 
 
@@ -426,6 +430,8 @@ FP8 = [
     _small("d64_g8_bs8_odd_scales", head_dim=64, num_q_heads=8, num_kv_heads=1, block_size=8,
            seed=140).fp8(k_scale=0.0517, v_scale=1.75, code_std=8.0),
     _small("ring_wrap_bs64", sink=2, window=16, prefill=(100, 37, 5), steps=40, block_size=64, seed=135).fp8(),
+    _small("ring_wrap_g4", num_q_heads=8, num_kv_heads=2, sink=2, window=16, prefill=(100, 37, 5), steps=40,
+           block_size=64, seed=141).fp8(),
     _small("hybrid_focus", num_layers=8, sw_window=64, sink=4, window=128, batch=3,
            prefill=(1000, 2500, 6000), steps=10, layer_kind=tuple(0 if i % 4 == 3 else 1 for i in range(8)),
            focus=True, seed=136).fp8(),
