@@ -143,11 +143,11 @@ def test_ctx128k_rho0125_fp8_kv_sampled():
     _check(*out, (0, 27), (0,))
 
 
-@pytest.mark.parametrize("group,kv", [(4, "bf16"), (4, "fp8"), (8, "bf16")])
+@pytest.mark.parametrize("group,kv", [(4, "bf16"), (4, "fp8"), (8, "bf16"), (8, "fp8")])
 def test_ctx128k_gqa_groups_sampled(group, kv):
     """The 128K workload with 32 or 64 query heads over the 8 KV heads (GQA
-    groups of 4 and 8: the paged passes on MFMA, the tail pool for bf16, the
-    ring passes' narrower geometries)."""
+    groups of 4 and 8, bf16 and FP8: paged and ring passes on MFMA, the tail
+    pool for bf16)."""
     wl = W.config(2).with_(num_q_heads=8 * group, rho=(0.5,))
     if kv == "fp8":
         wl = wl.fp8()
