@@ -16,6 +16,8 @@
 // per-lane reference maximum; the current token (position t, which the caches
 // do not hold yet) is one more row, read from k_cur / v_cur by the last split.
 // Ring (Local) passes use a wider geometry: one 16-byte chunk per lane and row.
+// GQA groups of 4 and 8 with bf16 or FP8 K/V compute both products on MFMA
+// (S^T = K Q^T, then O^T += V^T P^T with V transposed through LDS).
 // Long paged passes end with a pool of tiles that the splits of a (request,
 // KV head) take one at a time.  Each workgroup leaves one (o, m, l) partial per
 // query head, and one workgroup of each (request, KV head) merges them into the
