@@ -214,7 +214,8 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
 // SIMD without spilling; groups of 8 take a quarter of the vectors and twice
 // the passes, a tile half as tall.  Passes of bf16 and FP8 groups of 4 and 8
 // (MF) put both products on MFMA instead: lane l holds chunks 4j + l/16
-// of row l % 16 of each 16-row pass; each 8 of its elements (FP8 widened to
+// of row l % 16 of each 16-row pass (two passes per tile for FP8, so a tile
+// still carries 64 KiB of K and V); each 8 of its elements (FP8 widened to
 // bf16) are the A operand of one 16x16x32 bf16 form for S^T = K Q^T, the
 // matching query elements its B operand; the scores come out as the B
 // operand of the 16x16x16 form for O^T += V^T P^T, whose A operand (V
@@ -235,12 +236,12 @@ struct Geo {
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : MF ? 1 : (DT == ODA_FP8_E4M3 ? 2 : 1) * PASSES;  // passes per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * (MF ? 1 : PASSES);  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
   static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
-  static_assert(!MF || (LPR == 4 && RPP == 16 && NP == 1 && G <= 16 && QV == NV * QPV && QES == 2),
-                "MFMA pass: 16 rows of 4 lanes, one pass, bf16 queries");
+  static_assert(!MF || (LPR == 4 && RPP == 16 && G <= 16 && QV == NV * QPV && QES == 2),
+                "MFMA pass: 16 rows of 4 lanes, bf16 queries");
 };
 
 // One element of a stored K/V row and of a query row, widened to f32.
@@ -818,85 +819,88 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 
   auto process_tile = [&](TileRegs& R) {
     if constexpr (Gm::MF) {
-      if (SKIP && !R.live[0]) return;
-      if constexpr (SRC == kSrcRing) {  // membership in S^L_t: other slots may hold anything
-        bool in_local = R.valid[0] && R.row[0] == n_rows;
-        if (R.valid[0] && !in_local) ring_slot_position(rst, R.row[0], in_local);
-        R.valid[0] = in_local;
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
-          if (!in_local) R.v[0][j] = make_uint4(0, 0, 0, 0);
-      }
-      // S^T = K Q^T: lane l gets the scores of rows 4 (l / 16) + r of head l % 16
-      // (a row outside the sums may hold anything; its scores are dropped).
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NP; ++i) {  // 16 rows of each wave per pass
+        if (SKIP && !R.live[i]) continue;
+        if constexpr (SRC == kSrcRing) {  // membership in S^L_t: other slots may hold anything
+          bool in_local = R.valid[i] && R.row[i] == n_rows;
+          if (R.valid[i] && !in_local) ring_slot_position(rst, R.row[i], in_local);
+          R.valid[i] = in_local;
 #pragma unroll
-      for (int j = 0; j < QV; ++j) {  // the lane's row elements 8j .. 8j + 7
-        uint4 ka = R.k[0][j / QPV];
-        if constexpr (DT == ODA_FP8_E4M3) {
-          const uint32_t w0 = j % 2 ? ka.z : ka.x, w1 = j % 2 ? ka.w : ka.y;
-          ka = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
-                          fp8x2_to_bf16x2<true>(w1));
+          for (int j = 0; j < NV; ++j)
+            if (!in_local) R.v[i][j] = make_uint4(0, 0, 0, 0);
         }
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
-                                                     __builtin_bit_cast(bf16x8_t, qv[0][j]), sc, 0, 0, 0);
-      }
-      // The pass's V rows go to LDS as bf16 rows.
-      char* vt = s_vt + wave * 16 * VST;
+        // S^T = K Q^T: lane l gets the scores of rows 4 (l / 16) + r of head l % 16
+        // (a row outside the sums may hold anything; its scores are dropped).
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        char* dst = vt + rrow * VST + (j * LPR + sub) * EPV * 2;
-        if constexpr (DT == ODA_FP8_E4M3) {
-          const uint4 w = R.v[0][j];
-          *reinterpret_cast<uint4*>(dst) = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
-                                                      fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
-          *reinterpret_cast<uint4*>(dst + 16) = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
-                                                           fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = R.v[0][j];
+        for (int j = 0; j < QV; ++j) {  // the lane's row elements 8j .. 8j + 7
+          uint4 ka = R.k[i][j / QPV];
+          if constexpr (DT == ODA_FP8_E4M3) {
+            const uint32_t w0 = j % 2 ? ka.z : ka.x, w1 = j % 2 ? ka.w : ka.y;
+            ka = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                            fp8x2_to_bf16x2<true>(w1));
+          }
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                       __builtin_bit_cast(bf16x8_t, qv[0][j]), sc, 0, 0, 0);
         }
+        // The pass's V rows go to LDS as bf16 rows.
+        char* vt = s_vt + wave * 16 * VST;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          char* dst = vt + rrow * VST + (j * LPR + sub) * EPV * 2;
+          if constexpr (DT == ODA_FP8_E4M3) {
+            const uint4 w = R.v[i][j];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                                        fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+            *reinterpret_cast<uint4*>(dst + 16) = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                                             fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
+          } else {
+            *reinterpret_cast<uint4*>(dst) = R.v[i][j];
+          }
+        }
+        const uint64_t vm = __ballot(R.valid[i]);  // bit r: row r of the pass is in the sums
+        const int q4 = (lane >> 4) * 4;
+        float s[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[r] = (vm >> (q4 + r)) & 1 ? sc[r] * P.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[r]);
+        }
+        mx = quarters_max(mx);
+        if (mx > m_mf + kRescaleGap) {
+          const float alpha = m_mf == -INFINITY ? 0.f : fast_exp2(m_mf - mx);
+          l_mf *= alpha;
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi) acc_mf[mi] *= alpha;
+          m_mf = mx;
+        }
+        // P^T as a sum of two bf16 parts (the second holds what rounding the
+        // first lost), so the weights keep about 16 bits in the products.
+        i16x4_t ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w = s[r] == -INFINITY ? 0.f : fast_exp2(s[r] - m_mf);
+          const __bf16 wh = (__bf16)w;
+          ph[r] = __builtin_bit_cast(short, wh);
+          pl[r] = __builtin_bit_cast(short, (__bf16)(w - (float)wh));
+          l_mf += w;
+        }
+        // O^T += V^T P^T, 16 elements at a time: lane l reads element
+        // 16 mi + l % 16 of rows 4 (l / 16) + r.
+        const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+        i16x4_t va[MT];
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) va[mi][r] = (short)vt16[(q4 + r) * (VST / 2) + 16 * mi + lane % 16];
+          acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], ph, acc_mf[mi], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+          acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], pl, acc_mf[mi], 0, 0, 0);
       }
-      const uint64_t vm = __ballot(R.valid[0]);  // bit r: row r of the pass is in the sums
-      const int q4 = (lane >> 4) * 4;
-      float s[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r] = (vm >> (q4 + r)) & 1 ? sc[r] * P.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[r]);
-      }
-      mx = quarters_max(mx);
-      if (mx > m_mf + kRescaleGap) {
-        const float alpha = m_mf == -INFINITY ? 0.f : fast_exp2(m_mf - mx);
-        l_mf *= alpha;
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) acc_mf[mi] *= alpha;
-        m_mf = mx;
-      }
-      // P^T as a sum of two bf16 parts (the second holds what rounding the
-      // first lost), so the weights keep about 16 bits in the products.
-      i16x4_t ph, pl;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float w = s[r] == -INFINITY ? 0.f : fast_exp2(s[r] - m_mf);
-        const __bf16 wh = (__bf16)w;
-        ph[r] = __builtin_bit_cast(short, wh);
-        pl[r] = __builtin_bit_cast(short, (__bf16)(w - (float)wh));
-        l_mf += w;
-      }
-      // O^T += V^T P^T, 16 elements at a time: lane l reads element
-      // 16 mi + l % 16 of rows 4 (l / 16) + r.
-      const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
-      i16x4_t va[MT];
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) va[mi][r] = (short)vt16[(q4 + r) * (VST / 2) + 16 * mi + lane % 16];
-        acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], ph, acc_mf[mi], 0, 0, 0);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-        acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], pl, acc_mf[mi], 0, 0, 0);
     } else {
     if constexpr (SRC == kSrcRing) {
       // Membership in S^L_t; rows outside it never reach the sums (slots not
