@@ -61,14 +61,17 @@ def parse():
                     help="compute the recall scores on the device with the recall-head stand-in "
                          "(6144 -> 4608 -> 1, seeded weights, b2 set so that about rho of the steps fire)")
     ap.add_argument("--reps", type=int, default=1,
-                    help="timed repetitions of the K steps from the same state (value: the median)")
+                    help="timed repetitions of the whole measurement from the same state (value: the median)")
     ap.add_argument("--roofline-launches", type=int, default=56)
     ap.add_argument("--full-splits", type=int, default=0,
                     help="split-K ranges per (request, KV head) of Full passes (0: the library's choice)")
     ap.add_argument("--local-splits", type=int, default=0,
                     help="split-K ranges per (request, KV head) of ring passes (0: the library's choice)")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time rho=0, rho=1 and always-Full for the savings check")
+                    help="also time rho=0, rho=1 and always-Full for the savings check (always done for "
+                         "the 128K workload)")
+    ap.add_argument("--no-delta-f", action="store_true",
+                    help="skip the rho=0 / rho=1 / always-Full legs of the savings check")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -134,6 +137,22 @@ def kernel_sha() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
+def exact_rate_blocks(wl, K: int, max_blocks: int = 64) -> int:
+    """Blocks of K steps needed so that exactly rho of all timed steps fire
+    (scores drawn by the 'exact' mode: a seeded choice of round(rho * n) of n
+    steps).  rho * K need not be whole: with r blocks the choice is made over
+    r * K steps, r the least for which rho * r * K is whole (rho = 1/8 and
+    K = 20: two blocks, 5 of 40 steps fire).  1 for the other score modes."""
+    from fractions import Fraction
+    if wl.score_mode != "exact" or len(set(wl.rho)) != 1:
+        return 1
+    fr = Fraction(wl.rho[0]).limit_denominator(10 ** 6)
+    for r in range(1, max_blocks + 1):
+        if (fr * r * K).denominator == 1:
+            return r
+    return 1
+
+
 def build_workload(args):
     from gated_kv_access_amd import workloads as W
     base = W.config(args.config)
@@ -169,28 +188,31 @@ def main() -> int:
     B.load()
     base, K = build_workload(args)
     Wm = args.warmup
-    wl = base.with_(steps=Wm + K)
+    # Timed: r blocks of K steps, so that exactly rho of them fire.
+    nblk = exact_rate_blocks(base, K)
+    T = nblk * K
+    wl = base.with_(steps=Wm + T)
     pre = np.array(wl.prefill, dtype=np.int64)
-    log(f"workload {wl.name}: batch {wl.batch}, prefill {pre.min()}..{pre.max()}, warmup {Wm}, timed {K}, "
-        f"rho {wl.rho if len(wl.rho) < 5 else 'per request'}")
+    log(f"workload {wl.name}: batch {wl.batch}, prefill {pre.min()}..{pre.max()}, warmup {Wm}, timed {T} "
+        f"({nblk} block(s) of {K}), rho {wl.rho if len(wl.rho) < 5 else 'per request'}")
     if args.config == 3:
         free = torch.cuda.mem_get_info()[0]
-        need = float((pre + Wm + K).sum()) * wl.num_layers * wl.num_kv_heads * wl.head_dim * 2 * wl.esize
+        need = float((pre + Wm + T).sum()) * wl.num_layers * wl.num_kv_heads * wl.head_dim * 2 * wl.esize
         if need > 0.92 * free:
             log(f"paged cache of {need / 1e9:.0f} GB does not fit the {free / 1e9:.0f} GB free")
             return 1
     t0 = time.time()
     head = head_x = None
     if args.recall_head:
-        head, head_x = make_head(wl, Wm + K)
+        head, head_x = make_head(wl, Wm + T)
     dims = make_dims(wl, full_splits=args.full_splits, local_splits=args.local_splits,
                      recall_flops=head.flops if head else 0)
     st = DecodeState(wl, gen_device="cuda", host_cache=args.host_kv, dims=dims)
     st.prefill()
     q = W.gen_queries(wl, "cuda")
     k_new, v_new = st.decode_inputs()
-    sc = np.concatenate([W.gen_scores(wl.with_(steps=Wm)), W.gen_scores(wl.with_(steps=K))], 0) \
-        if Wm > 0 else W.gen_scores(wl.with_(steps=K))
+    sc = np.concatenate([W.gen_scores(wl.with_(steps=Wm)), W.gen_scores(wl.with_(steps=T))], 0) \
+        if Wm > 0 else W.gen_scores(wl.with_(steps=T))
     scores = torch.from_numpy(sc).cuda()
     log(f"setup {time.time() - t0:.1f}s")
 
@@ -207,29 +229,35 @@ def main() -> int:
         torch.cuda.synchronize()
 
     times = []
+    block_ms = []
     acct = None
     for rep in range(max(1, args.reps)):
         if rep:
             restore()
         acct0 = r.counters.clone()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        r.replay(K)
-        end.record()
-        torch.cuda.synchronize()
-        times.append(start.elapsed_time(end))
+        blocks = []
+        for _ in range(nblk):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            r.replay(K)
+            end.record()
+            torch.cuda.synchronize()
+            blocks.append(start.elapsed_time(end))
+        times.append(sum(blocks))
         if acct is None:
             acct = (r.counters - acct0).cpu().numpy().sum(0)
+            block_ms = blocks
     if st.device_error() != 0:
         log(f"device error word {st.device_error()}")
         return 1
-    ms = statistics.median(times)
+    ms = statistics.median(times)  # for T steps
     f = dict(zip(B.ACCT_FIELDS, acct.tolist()))
-    steps_per_s = K / (ms / 1e3)
+    steps_per_s = T / (ms / 1e3)
     kv_gbps = f["kv_bytes"] / (ms / 1e3) / 1e9
-    log(f"timed {K} steps in {ms:.1f} ms (median of {len(times)}): {steps_per_s:.1f} steps/s, "
-        f"{kv_gbps:.0f} GB/s effective KV, {f['full_calls']} Full calls")
+    rho_realised = f["full_calls"] / (T * wl.batch)
+    log(f"timed {T} steps in {ms:.1f} ms (median of {len(times)}): {steps_per_s:.1f} steps/s, "
+        f"{kv_gbps:.0f} GB/s effective KV, {f['full_calls']} Full calls (rho realised {rho_realised:.4f})")
 
     roofline = roofline_leg(args, st, wl, q, k_new, v_new)
     copy_us, copy_gbps = copy_rate()
@@ -247,8 +275,9 @@ def main() -> int:
     extra = {}
     if head is not None:
         extra["recall_head"] = recall_head_leg(head, head_x, wl.batch)
-    if args.sweep:
-        extra.update(sweep(st, wl, q, k_new, v_new, K, Wm, start_len))
+    if (args.sweep or args.config == 2) and not args.no_delta_f:
+        legs = sweep(st, wl, q, k_new, v_new, K, Wm, start_len)
+        extra["delta_f"] = delta_f_check(legs, ms / T * 1e3, f, wl, rho_realised, kv_gbps, roofline)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -264,7 +293,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms / K, 4),
+        "ms_per_step": round(ms / T, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -274,7 +303,9 @@ def main() -> int:
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "prefill": int(pre[0]) if wl.batch == 1 else [int(pre.min()), int(pre.max())],
                    "sink": wl.sink, "window": wl.window, "block_size": wl.block_size,
-                   "rho": list(wl.rho) if len(wl.rho) > 1 else wl.rho[0], "kv_dtype": wl.dtype,
+                   "rho": list(wl.rho) if len(wl.rho) > 1 else wl.rho[0],
+                   "rho_realised": round(rho_realised, 6), "timed_steps": T, "timed_blocks": nblk,
+                   "kv_dtype": wl.dtype,
                    "sliding_layers": len(wl.sliding_layers), "focus": bool(wl.focus),
                    "paged_history": "pinned host memory" if args.host_kv else "HBM",
                    "recall_score": "device recall head" if head is not None else "staged input",
@@ -288,6 +319,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    res["ms_per_block"] = [round(t, 3) for t in block_ms]
     if len(times) > 1:
         res["ms_per_rep"] = [round(t, 3) for t in times]
     res.update(extra)
@@ -395,8 +427,9 @@ def roofline_leg(args, st, wl, q, k_new, v_new):
 
 
 def sweep(st, wl, q, k_new, v_new, K, Wm, start_len):
-    """rho = 0, rho = 1 and always-Full over the same K steps, for the step-time
-    ratio against the FLOP prediction of the per-step savings equation."""
+    """rho = 0, rho = 1 and always-Full over K steps from the timed run's start,
+    for the step-time ratio against the FLOP prediction of the per-step savings
+    equation.  Returns microseconds per step of each leg."""
     import torch
 
     from gated_kv_access_amd import binding as B
@@ -452,7 +485,45 @@ def sweep(st, wl, q, k_new, v_new, K, Wm, start_len):
 
     ms_full = time_runner(FullOnly(), "always-Full")
     out["us_per_step_full_only"] = round(ms_full * 1e3, 2)
-    return {"sweep": out}
+    return out
+
+
+def delta_f_check(legs, us_rho, f, wl, rho_realised, kv_gbps, roofline):
+    """The savings check of the per-step savings equation (picx.dev summary,
+    "Computational Savings"): the measured step-time ratio against always-Full,
+    R = T(rho) / T(always-Full), beside the FLOP ratio the counters give,
+    R_hat = sum(F_Local + F_Recall + a_t F_Full(t)) / sum(F_Full(t)); the affine
+    model T(rho) = T(0) + rho (T(1) - T(0)); and the shortfall against 70% of
+    HBM peak on the KV bytes read, at always-Full, rho = 1 and the timed rho."""
+    t0, t1, tf = legs["us_per_step_rho0"], legs["us_per_step_rho1"], legs["us_per_step_full_only"]
+    r_hat = (f["f_local"] + f["f_recall"] + f["f_full_taken"]) / f["f_full_always"]
+    r_meas = us_rho / tf
+    affine = t0 + rho_realised * (t1 - t0)
+    # KV bytes per step of the legs, from the counters' attended positions
+    # (F counts 4 * Hq * d per attended position and layer; a position and
+    # layer is Hkv * d * 2 * element-size bytes of K and V)
+    per_step = wl.batch / f["steps"]
+    per_pos = wl.num_kv_heads * wl.head_dim * 2 * wl.esize
+    fpp = 4 * wl.num_q_heads * wl.head_dim
+    full_b = f["f_full_always"] / fpp * per_pos * per_step
+    loc_b = f["f_local"] / fpp * per_pos * per_step
+    frac = {"always_full": full_b / (tf * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "rho1": (full_b + loc_b) / (t1 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "timed_rho": kv_gbps / HBM_PEAK_GBPS,
+            "full_pass_kernel": roofline["frac"]}
+    out = {"us_per_step_rho0": t0, "us_per_step_rho1": t1, "us_per_step_full_only": tf,
+           "us_per_step_timed": round(us_rho, 2), "rho_realised": round(rho_realised, 6),
+           "R_measured": round(r_meas, 5), "R_hat": round(r_hat, 5),
+           "R_over_R_hat": round(r_meas / r_hat, 4),
+           "fixed_cost_us": round(us_rho - r_hat * tf, 2),
+           "affine_predicted_us": round(affine, 2), "affine_residual_us": round(us_rho - affine, 2),
+           "hbm_frac": {k: round(v, 4) for k, v in frac.items()},
+           "target_hbm_frac": 0.70,
+           "target_met": {k: bool(v >= 0.70) for k, v in frac.items()}}
+    log(f"delta-F: R = {r_meas:.4f} vs R_hat = {r_hat:.4f}; T(0) {t0:.1f} us, T(1) {t1:.1f} us, "
+        f"always-Full {tf:.1f} us; affine residual {us_rho - affine:+.1f} us; "
+        f"HBM fractions {', '.join(f'{k} {v:.3f}' for k, v in frac.items())} (target 0.70)")
+    return out
 
 
 def cpu_baseline(st, wl, q, rho, n_layers):

@@ -86,7 +86,6 @@ oda_status make_plan(const oda_dims* d, Plan* p) {
   p->scale_log2 = scale * k_scale * 1.44269504088896340736f;
   p->v_scale = d->v_scale > 0.f ? d->v_scale : 1.f;
   p->tile_rows = oda::tile_rows_for(p->dtype, p->D, oda::kSrcPaged, p->G);
-  p->ring_tile_rows = oda::tile_rows_for(p->dtype, p->D, oda::kSrcRing, p->G);
   return ODA_OK;
 }
 

@@ -28,8 +28,7 @@ struct Plan {
   uint8_t kind[ODA_MAX_LAYERS];
   int16_t kidx[ODA_MAX_LAYERS];  // rank of the layer among layers of its kind
   int32_t full_splits, local_splits, sw_splits;
-  int32_t tile_rows;       // rows one workgroup consumes per iteration: paged passes
-  int32_t ring_tile_rows;  // the same for ring passes
+  int32_t tile_rows;  // rows one workgroup consumes per iteration of a paged pass
   float scale_log2;   // softmax scale * k_scale * log2(e)
   float v_scale;
   int64_t recall_flops;

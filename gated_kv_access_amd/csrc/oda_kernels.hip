@@ -161,6 +161,18 @@ __device__ __forceinline__ float quarters_sum(float v) {
 // fp32 overflow, and the result is exact whatever the reference is.
 constexpr float kRescaleGap = 8.f;
 
+// Orders one wave's LDS accesses around an exchange between its lanes (the
+// stores of some lanes before the loads of others, and those loads before the
+// next stores to the same rows).  A wave's LDS instructions already execute in
+// order; the fence makes the ordering part of the program rather than a
+// property of the hardware, and the barrier keeps the compiler from moving
+// accesses across it.  Neither emits an instruction.
+__device__ __forceinline__ void wave_lds_exchange() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Device-coherent (agent scope) stores and loads of the split partials.  On
 // gfx950 they carry the device scope bit, so a partial written on one XCD is
 // read correctly on another without writing back or invalidating any L2.
@@ -859,6 +871,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
             *reinterpret_cast<uint4*>(dst) = R.v[i][j];
           }
         }
+        wave_lds_exchange();  // the pass's V rows are in LDS before any lane reads them transposed
         const uint64_t vm = __ballot(R.valid[i]);  // bit r: row r of the pass is in the sums
         const int q4 = (lane >> 4) * 4;
         float s[4];
@@ -900,6 +913,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi)
           acc_mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mi], pl, acc_mf[mi], 0, 0, 0);
+        wave_lds_exchange();  // every transposed read is done before the next pass overwrites the rows
       }
     } else {
     if constexpr (SRC == kSrcRing) {
@@ -1700,18 +1714,34 @@ int launch_attention_d(const Plan& p, const AttnParams& a, int32_t batch, oda_st
 
 }  // namespace
 
+// Rows per tile of the kernel built for (dtype, d, source, group): the same
+// Geo<> instantiation the launch dispatches to (f32 groups of 8 exist for
+// d = 64 only; the host reports the other case unsupported before asking).
 template <int SRC, int G>
 int tile_rows_src(int32_t dtype, int32_t head_dim) {
   if (dtype == ODA_BF16) return head_dim == 128 ? Geo<ODA_BF16, 128, SRC, G>::TILE : Geo<ODA_BF16, 64, SRC, G>::TILE;
   if (dtype == ODA_FP8_E4M3)
-    return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128, SRC>::TILE : Geo<ODA_FP8_E4M3, 64, SRC>::TILE;
-  return head_dim == 128 ? Geo<ODA_F32, 128, SRC, (G >= 8 ? 1 : G)>::TILE : Geo<ODA_F32, 64, SRC, G>::TILE;
+    return head_dim == 128 ? Geo<ODA_FP8_E4M3, 128, SRC, G>::TILE : Geo<ODA_FP8_E4M3, 64, SRC, G>::TILE;
+  if constexpr (kGroup8Built<ODA_F32, 128> || G < 8) {
+    if (head_dim == 128) return Geo<ODA_F32, 128, SRC, G>::TILE;
+  }
+  return head_dim == 128 ? 0 : Geo<ODA_F32, 64, SRC, G>::TILE;
+}
+
+template <int SRC>
+int tile_rows_g(int32_t dtype, int32_t head_dim, int32_t group) {
+  switch (group) {
+    case 1: return tile_rows_src<SRC, 1>(dtype, head_dim);
+    case 2: return tile_rows_src<SRC, 2>(dtype, head_dim);
+    case 4: return tile_rows_src<SRC, 4>(dtype, head_dim);
+    case 8: return tile_rows_src<SRC, 8>(dtype, head_dim);
+    default: return 0;
+  }
 }
 
 int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source, int32_t group) {
-  if (group >= 8)
-    return source == kSrcRing ? tile_rows_src<kSrcRing, 8>(dtype, head_dim) : tile_rows_src<kSrcPaged, 8>(dtype, head_dim);
-  return source == kSrcRing ? tile_rows_src<kSrcRing, 1>(dtype, head_dim) : tile_rows_src<kSrcPaged, 1>(dtype, head_dim);
+  return source == kSrcRing ? tile_rows_g<kSrcRing>(dtype, head_dim, group)
+                            : tile_rows_g<kSrcPaged>(dtype, head_dim, group);
 }
 
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {

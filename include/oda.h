@@ -161,7 +161,10 @@ oda_status oda_prefill_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                           void* workspace, size_t workspace_bytes, oda_stream stream);
 
 /* Rebuilds every gated layer's ring (and ring_pos) from the paged cache for
- * the committed positions 1..seq_len[b]. */
+ * the committed positions 1..seq_len[b].  The ring is the persistent Local KV
+ * workspace of the picx.dev summary, section "Efficient Execution"; it holds
+ * the s initial positions and the last w positions that S^L_t reads
+ * (section "Local-First Decoding", access-set equation). */
 oda_status oda_ring_init(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                          void* workspace, size_t workspace_bytes, oda_stream stream);
 
@@ -174,18 +177,24 @@ oda_status oda_commit_kv(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                          const void* k_new, const void* v_new,
                          void* workspace, size_t workspace_bytes, oda_stream stream);
 
-/* The Local pass of one layer for every active request: softmax attention of
- * q [batch][Hq][d] over S^L_t (gated layer: sinks + window, from the ring;
- * sliding layer: its window) where position t is k_cur/v_cur [batch][Hkv][d].
- * Writes out [batch][Hq][d] and lse [batch][Hq] (natural log; nullable). */
+/* The Local pass of one layer for every active request (picx.dev summary,
+ * section "Local-First Decoding": every step first runs the Local access mode,
+ * F^L over S^L_t; the ring it reads is the one of section "Efficient
+ * Execution"): softmax attention of q [batch][Hq][d] over S^L_t (gated layer:
+ * sinks + window, from the ring; sliding layer: its window) where position t
+ * is k_cur/v_cur [batch][Hkv][d].  Writes out [batch][Hq][d] and lse
+ * [batch][Hq] (natural log; nullable). */
 oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
                             const void* q, const void* k_cur, const void* v_cur,
                             float* out, float* lse,
                             void* workspace, size_t workspace_bytes, oda_stream stream);
 
-/* The gate plus the Full pass of one layer.  A request fires iff
- * recall_score[b] > theta (strict; NaN never fires; inactive slots never
- * fire).  Fired requests, compacted in ascending order, attend S^F_t
+/* The gate plus the Full pass of one layer (picx.dev summary, section
+ * "Local-First Decoding": if q_t > theta the step is recomputed with the Full
+ * access set S^F_t = {1..t}, otherwise the Local result is accepted; the
+ * decision stays on the device as in section "Efficient Execution").  A
+ * request fires iff recall_score[b] > theta (strict; NaN never fires;
+ * inactive slots never fire).  Fired requests, compacted in ascending order, attend S^F_t
  * (or S^L_t U [a,b) when dims.focus; sliding layers: their window) over the
  * paged cache with position t from k_cur/v_cur, and their rows of out / lse
  * are overwritten; rows of requests that did not fire are left as they are
@@ -207,9 +216,14 @@ oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                     int32_t* call_count, int64_t* full_calls, int64_t* counters,
                     oda_stream stream);
 
-/* One whole decode step for every active request, in this order: the Local
- * pass of every layer, the gate (with accounting), the Full pass of every
- * layer for the fired requests, then the fused commit.  q_local / q_full
+/* One whole decode step for every active request, in the order of the
+ * picx.dev summary, section "Local-First Decoding" (Local first, then the
+ * recall-score gate, then Full only where q_t > theta), run as section
+ * "Efficient Execution" describes (device-side conditional Full pass, fused
+ * cross-layer KV commit; learnaivisually explainer, runtime paragraph: the
+ * recalled step still pays the Local attempt): the Local pass of every layer,
+ * the gate (with accounting), the Full pass of every layer for the fired
+ * requests, then the fused commit.  q_local / q_full
  * [L][batch][Hq][d] (q_full NULL: reuse q_local), k_new / v_new
  * [L][batch][Hkv][d], out [L][batch][Hq][d] (the accepted result), lse
  * [L][batch][Hq] (nullable).  Capture it once into a HIP graph and replay it
@@ -221,9 +235,12 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                     int64_t* full_calls, int64_t* counters,
                     void* workspace, size_t workspace_bytes, oda_stream stream);
 
-/* The positions layer `layer` would attend for request b in the given mode
- * (0 Local, 1 Full) at t = seq_len[b]+1, derived by the same device index
- * code the attention kernels use: *count is set to the set size and the
+/* The access sets of the picx.dev summary, section "Local-First Decoding"
+ * (S^L_t = {1..min(s,t)} U {max(1,t-w+1)..t}, S^F_t = {1..t}; focus and
+ * sliding variants as for oda_decode_full_gated): the positions layer `layer`
+ * would attend for request b in the given mode (0 Local, 1 Full) at
+ * t = seq_len[b]+1, derived by the same device index code the attention
+ * kernels use: *count is set to the set size and the
  * members are written, in no particular order, to positions [capacity].
  * Sets ODA_DEVERR_OUT_CAPACITY if capacity is too small. */
 oda_status oda_access_set(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t b,

@@ -52,3 +52,19 @@ def test_kernel_hash_ignores_comments_and_blank_lines(tmp_path, monkeypatch):
     assert bench.kernel_sha() == h
     monkeypatch.setattr(bench, "KERNEL_SRC", str(changed))
     assert bench.kernel_sha() != h
+
+
+def test_exact_rate_blocks_make_the_timed_rate_exact():
+    """rho * (blocks * K) is whole for every K, so exactly rho of the timed steps fire."""
+    import numpy as np
+
+    from gated_kv_access_amd import workloads as W
+    wl, _ = bench.build_workload(_args())
+    for K, want in ((1024, 1), (20, 2), (5, 8), (8, 1), (12, 2), (1, 8)):
+        r = bench.exact_rate_blocks(wl, K)
+        assert r == want, (K, r)
+        T = r * K
+        fired = int((W.gen_scores(wl.with_(steps=T)) > 0).sum())
+        assert fired == T // 8 and fired * 8 == T
+    # Bernoulli draws (the other score modes) are timed in one block
+    assert bench.exact_rate_blocks(W.config(1), 20) == 1

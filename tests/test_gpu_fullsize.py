@@ -47,12 +47,23 @@ def _run_and_sample(wl, steps, sample_steps, sample_layers, sample_requests, hos
     return wl, st, q, scores, r, rec
 
 
-def _check(wl, st, q, scores, r, rec, sample_layers, sample_requests):
+def _check(wl, st, q, scores, r, rec, sample_layers, sample_requests, each_request_both=True):
+    """each_request_both: every sampled request must have at least one fired and
+    one unfired sampled step (else: the samples as a whole must), so that both
+    the Full pass over the paged cache and the accepted Local pass are compared
+    with the oracle whatever the seeds."""
     cfg = oracle_cfg(wl)
     focus = st.focus_range.cpu().numpy()
     steps = wl.steps
     # integer results over every step: gate decisions, totals, counters
     fired = scores > 0
+    ks_sampled = sorted(rec)
+    per_req = [(int(fired[ks_sampled, b].sum()), int((~fired[ks_sampled, b]).sum())) for b in sample_requests]
+    if each_request_both:
+        for b, (nf, nu) in zip(sample_requests, per_req):
+            assert nf >= 1 and nu >= 1, (wl.name, "request", b, "sampled steps", ks_sampled, "fired", nf, "unfired", nu)
+    else:
+        assert sum(n for n, _ in per_req) >= 1 and sum(n for _, n in per_req) >= 1, (wl.name, ks_sampled, per_req)
     for k, (_, count, clist) in rec.items():
         want = np.flatnonzero(fired[k])
         assert count == want.size
@@ -71,6 +82,7 @@ def _check(wl, st, q, scores, r, rec, sample_layers, sample_requests):
     G = wl.num_q_heads // wl.num_kv_heads
     atol, rtol = TOL[wl.dtype]
     worst = 0.0
+    n_fired = n_unfired = 0
     for li, l in enumerate(sample_layers):
         kind = wl.kinds[l]
         for bi, b in enumerate(sample_requests):
@@ -92,14 +104,19 @@ def _check(wl, st, q, scores, r, rec, sample_layers, sample_requests):
                     mabs = float(np.abs(diff).max())
                     rel = float(np.linalg.norm(diff) / np.linalg.norm(want))
                     worst = max(worst, mabs)
-                    assert mabs <= atol and rel <= rtol, (wl.name, k, l, b, mabs, rel)
-    say(f"{wl.name}: sampled outputs within bars, worst max-abs {worst:.3e}")
+                    assert mabs <= atol and rel <= rtol, (wl.name, k, l, b, bool(fired[k, b]), mabs, rel)
+                    if fired[k, b]:
+                        n_fired += 1
+                    else:
+                        n_unfired += 1
+    say(f"{wl.name}: sampled outputs within bars, worst max-abs {worst:.3e}; "
+        f"{n_fired} fired (Full-pass) and {n_unfired} unfired (Local-pass) (step, layer, request) samples")
 
 
 def test_ctx16k_rho041_every_step_run_sampled_outputs():
     wl = W.config(1)
     steps = wl.steps
-    samp = {0, 1, 57, 128, steps - 1}
+    samp = {0, 1, 2, 57, 128, steps - 1}  # steps 1 and 2 fire
     out = _run_and_sample(wl, steps, samp, (0, 13, 27), (0,))
     _check(*out, (0, 13, 27), (0,))
 
@@ -107,8 +124,8 @@ def test_ctx16k_rho041_every_step_run_sampled_outputs():
 def test_ctx128k_rho0125_sampled():
     wl = W.config(2)
     steps = 48
-    out = _run_and_sample(wl, steps, {0, 5, 23, steps - 1}, (0, 27), (0,))
-    wl2, _, _, scores, _, _ = out
+    # with these seeds steps 2, 8, 13, 36, 44 and 46 fire
+    out = _run_and_sample(wl, steps, {0, 2, 8, 23, 46, steps - 1}, (0, 27), (0,))
     _check(*out, (0, 27), (0,))
 
 
@@ -123,15 +140,16 @@ def test_batched32_mixed_lengths_sampled():
     need = float((lens + steps).sum()) * 28 * 8 * 128 * 2 * 2
     if need > 0.92 * free:
         pytest.skip(f"paged cache of {need / 1e9:.0f} GB does not fit the {free / 1e9:.0f} GB free")
-    out = _run_and_sample(wl, steps, {0, steps - 1}, (0, 27), tuple(picks))
-    _check(*out, (0, 27), tuple(picks))
+    out = _run_and_sample(wl, steps, {0, 1, steps - 1}, (0, 27), tuple(picks))
+    # the picks include a request that never fires and one that always does
+    _check(*out, (0, 27), tuple(picks), each_request_both=False)
 
 
 @pytest.mark.parametrize("focus", [True, False], ids=["fire_focus", "fire_full"])
 def test_hybrid_sliding_and_focus_sampled(focus):
     wl = W.config(4).with_(focus=focus)
     steps = 10
-    out = _run_and_sample(wl, steps, {0, steps - 1}, (2, 3, 31), (0, 5))
+    out = _run_and_sample(wl, steps, {0, 3, steps - 1}, (2, 3, 31), (0, 5))  # request 0 fires at 3, 9; 5 at 3
     _check(*out, (2, 3, 31), (0, 5))
 
 
@@ -139,7 +157,7 @@ def test_ctx128k_rho0125_fp8_kv_sampled():
     """The 128K workload with an E4M3 KV cache (per-tensor scales 1/16)."""
     wl = W.config(2).fp8()
     steps = 48
-    out = _run_and_sample(wl, steps, {0, 7, steps - 1}, (0, 27), (0,))
+    out = _run_and_sample(wl, steps, {0, 2, 7, 13, steps - 1}, (0, 27), (0,))  # 2 and 13 fire
     _check(*out, (0, 27), (0,))
 
 
@@ -159,7 +177,7 @@ def test_ctx128k_gqa_groups_sampled(group, kv):
 def test_hybrid_focus_fp8_kv_sampled():
     wl = W.config(4).fp8()
     steps = 8
-    out = _run_and_sample(wl, steps, {0, steps - 1}, (3, 31), (0, 7))
+    out = _run_and_sample(wl, steps, {0, 1, 4, steps - 1}, (3, 31), (0, 7))  # request 0 fires at 1, 7 at 4
     _check(*out, (3, 31), (0, 7))
 
 
