@@ -453,7 +453,7 @@ def sweep(st, wl, q, k_new, v_new, K, Wm, start_len):
         return ms / K
 
     for label, val in (("rho0", -1.0), ("rho1", 1.0)):
-        sc = torch.full((Wm + K, Bn), val, dtype=torch.float32, device="cuda")
+        sc = torch.full((q.shape[0], Bn), val, dtype=torch.float32, device="cuda")
         r = StepRunner(st, q, k_new, v_new, sc, want_lse=False)
         r.step_counter[0] = Wm
         out[f"us_per_step_{label}"] = round(time_runner(r, label) * 1e3, 2)
