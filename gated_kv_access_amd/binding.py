@@ -26,6 +26,7 @@ DEVERR_CAPACITY, DEVERR_BLOCK_ID, DEVERR_OUT_CAPACITY, DEVERR_MERGE_WAIT = 1, 2,
 # Every symbol include/oda.h declares.
 EXPORTS = ("oda_workspace_size", "oda_workspace_init", "oda_prefill_kv", "oda_ring_init",
            "oda_commit_kv", "oda_decode_local", "oda_decode_full_gated", "oda_gate", "oda_step",
+           "oda_step_static",
            "oda_access_set", "oda_stage_step", "oda_advance_counter", "oda_host_kv_pointer",
            "oda_recall_workspace_size", "oda_recall_workspace_init", "oda_recall_scores", "oda_step_recall",
            "oda_status_string")
@@ -94,6 +95,7 @@ def load(path: str = LIB_PATH):
         "oda_decode_full_gated": (I32, [D, K, I32, I32, P, P, P, P, F, P, P, P, P, P, SZ, P]),
         "oda_gate": (I32, [D, K, I32, P, F, P, P, P, P, P]),
         "oda_step": (I32, [D, K, I32, P, P, P, P, P, F, P, P, P, P, P, P, P, SZ, P]),
+        "oda_step_static": (I32, [D, K, I32, P, P, P, P, P, F, P, P, P, P, P, P, P]),
         "oda_access_set": (I32, [D, K, I32, I32, I32, P, I64, P, P, SZ, P]),
         "oda_stage_step": (I32, [I32, P, P, P, P, I64, P]),
         "oda_advance_counter": (I32, [P, P]),
@@ -193,6 +195,14 @@ def step(dims, kv, batch, q_local, q_full, k_new, v_new, recall_score, theta, ou
         ctypes.byref(dims), ctypes.byref(kv), batch, _p(q_local), _p(q_full), _p(k_new), _p(v_new),
         _p(recall_score), float(theta), _p(out), _p(lse), _p(call_list), _p(call_count),
         _p(full_calls), _p(counters), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def step_static(dims, kv, batch, q_local, q_full, k_new, v_new, recall_score, theta, out, lse, call_list,
+                call_count, full_calls, counters, stream=None) -> None:
+    _check("oda_step_static", load().oda_step_static(
+        ctypes.byref(dims), ctypes.byref(kv), batch, _p(q_local), _p(q_full), _p(k_new), _p(v_new),
+        _p(recall_score), float(theta), _p(out), _p(lse), _p(call_list), _p(call_count),
+        _p(full_calls), _p(counters), _stream(stream)))
 
 
 def access_set(dims, kv, layer, b, mode, positions, count, ws, stream=None) -> None:

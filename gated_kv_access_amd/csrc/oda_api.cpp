@@ -163,6 +163,7 @@ struct Ctx {
   WsLayout ws;
   char* base;
   uint32_t* err;
+  bool ticket_only = false;  // merge by ticket in every pass (the static scratch holds no empty-slot marks)
 };
 
 oda_status prepare(const oda_dims* dims, int32_t batch, void* workspace, size_t ws_bytes, Ctx* c,
@@ -263,7 +264,7 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   // static splits: the pool measured 3% slower for them at 128K (and no faster
   // at 96K or 160K), where it gains 3% for bf16.
   const bool one_round = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits;
-  a.merge_mode = one_round ? oda::kMergePoll : oda::kMergeTicket;
+  a.merge_mode = one_round && !c.ticket_only ? oda::kMergePoll : oda::kMergeTicket;
   a.claims = one_round && p.dtype != ODA_FP8_E4M3 ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
@@ -290,15 +291,21 @@ oda_status check_head_ws(const oda_recall_head* h, int32_t batch, void* ws, size
 // One decode step: Local pass of every layer; the recall head when one is
 // given (writing recall_score); the gate; the Full pass of every layer for the
 // fired requests; the fused commit.
+oda_status check_step(const Ctx& c, const oda_kv* kv, const void* q_local, const void* q_full,
+                      const void* k_new, const void* v_new, const float* recall_score, float theta,
+                      const float* out) {
+  if (!q_local || !k_new || !v_new || !recall_score || !out || isnan(theta)) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q_local) || (q_full && !aligned16(q_full)) || !aligned16(k_new) || !aligned16(v_new))
+    return ODA_ERR_INVALID_ARG;
+  return check_kv(c.plan, kv, true, true);
+}
+
 oda_status run_step(const Ctx& c, const oda_kv* kv, int32_t batch, const void* q_local, const void* q_full,
                     const void* k_new, const void* v_new, const oda_recall_head* head, const void* head_x,
                     void* head_ws, float* recall_score, float theta, float* out, float* lse,
                     int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
                     oda_stream stream) {
-  if (!q_local || !k_new || !v_new || !recall_score || !out || isnan(theta)) return ODA_ERR_INVALID_ARG;
-  if (!aligned16(q_local) || (q_full && !aligned16(q_full)) || !aligned16(k_new) || !aligned16(v_new))
-    return ODA_ERR_INVALID_ARG;
-  oda_status st = check_kv(c.plan, kv, true, true);
+  oda_status st = check_step(c, kv, q_local, q_full, k_new, v_new, recall_score, theta, out);
   if (st != ODA_OK) return st;
   if (batch == 0) return ODA_OK;
   const Plan& p = c.plan;
@@ -445,6 +452,35 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
   if (st != ODA_OK) return st;
   if (!recall_score) return ODA_ERR_INVALID_ARG;
+  return run_step(c, kv, batch, q_local, q_full, k_new, v_new, nullptr, nullptr, nullptr,
+                  const_cast<float*>(recall_score), theta, out, lse, call_list, call_count, full_calls, counters,
+                  stream);
+}
+
+oda_status oda_step_static(const oda_dims* dims, const oda_kv* kv, int32_t batch, const void* q_local,
+                           const void* q_full, const void* k_new, const void* v_new,
+                           const float* recall_score, float theta, float* out, float* lse,
+                           int32_t* call_list, int32_t* call_count, int64_t* full_calls, int64_t* counters,
+                           oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, nullptr, 0, &c, false);
+  if (st != ODA_OK) return st;
+  if (c.ws.total > oda::kStaticScratchBytes) return ODA_ERR_WORKSPACE;
+  st = check_step(c, kv, q_local, q_full, k_new, v_new, recall_score, theta, out);
+  if (st != ODA_OK) return st;
+  if (batch == 0) return ODA_OK;
+  void* scr = nullptr;
+  if (oda::static_scratch(&scr) != 0) return ODA_ERR_HIP;
+  c.base = static_cast<char*>(scr);
+  c.err = reinterpret_cast<uint32_t*>(c.base + c.ws.err_off);
+  c.ticket_only = true;
+  // The scratch keeps whatever the last call on this GPU left: the words that
+  // must read zero (error word, call list and count, tickets, tail-tile
+  // counters, commit tickets) are cleared by a kernel, not a memset, so the
+  // call may be captured into a graph.  Ticket merges read partials only
+  // after every split has stored its own, so the partial slots need no
+  // preparation.
+  if (oda::launch_clear(scr, c.ws.part_o_off, stream)) return ODA_ERR_HIP;
   return run_step(c, kv, batch, q_local, q_full, k_new, v_new, nullptr, nullptr, nullptr,
                   const_cast<float*>(recall_score), theta, out, lse, call_list, call_count, full_calls, counters,
                   stream);

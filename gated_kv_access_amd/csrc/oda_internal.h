@@ -128,6 +128,11 @@ int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float*
                   oda_stream s);
 // Device address of pinned host memory: 0, 1 (not pinned host memory) or 2 (runtime error).
 int host_device_pointer(void* host_ptr, void** device_ptr);
+// Bytes of the static scratch that oda_step_static uses as its workspace.
+constexpr size_t kStaticScratchBytes = ODA_STATIC_SCRATCH_BYTES;
+// Device address of this GPU's copy of that scratch (taken once per device,
+// with the device current): 0, or 1 (no current device) / 2 (runtime error).
+int static_scratch(void** ptr);
 // Rows per workgroup iteration for the attention kernel built for (dtype, d, source, group).
 int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source, int32_t group);
 

@@ -28,6 +28,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "oda_internal.h"
 
 namespace oda {
@@ -2139,6 +2141,39 @@ int launch_recall(const oda_recall_head& h, int32_t batch, const void* x, float*
   const size_t lds = (size_t)chunk * row_bytes;
   hipLaunchKernelGGL(recall_kernel, dim3(recall_groups(h.hidden)), dim3(kGroupThreads), lds, s, P);
   return (int)hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// static scratch of the step entry point that allocates nothing
+
+// The workspace of oda_step_static: one copy per GPU, held from the library's
+// load until the process ends.  In host code `scratch` names a host-side
+// stand-in, never its device copy: its device address is taken once per
+// device with hipGetSymbolAddress (that device current) and only that address
+// is used afterwards.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+int static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return 2;
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int host_device_pointer(void* host_ptr, void** device_ptr) {

@@ -235,6 +235,27 @@ oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch,
                     int64_t* full_calls, int64_t* counters,
                     void* workspace, size_t workspace_bytes, oda_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): oda_step
+ * with no caller workspace.  Its workspace is a static device array of
+ * ODA_STATIC_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends; the call allocates nothing and calls no allocating routine.
+ * Returns ODA_ERR_WORKSPACE before any launch when the workspace this dims and
+ * batch need (oda_workspace_size) exceed that size.  Every call on a GPU
+ * shares that GPU's array and starts with one small kernel that clears the
+ * words which must read zero, so calls that may overlap on one GPU (other
+ * streams or threads) race and must not be made.  Device-side errors skip the
+ * affected request as in oda_step but are not reported (the error word lives
+ * in the array).  Every pass merges its split partials by ticket, so outputs
+ * may differ from oda_step's in the last bits.  Other arguments and results
+ * as for oda_step. */
+enum { ODA_STATIC_SCRATCH_BYTES = 4 << 20 };
+oda_status oda_step_static(const oda_dims* dims, const oda_kv* kv, int32_t batch,
+                           const void* q_local, const void* q_full, const void* k_new,
+                           const void* v_new, const float* recall_score, float theta,
+                           float* out, float* lse, int32_t* call_list, int32_t* call_count,
+                           int64_t* full_calls, int64_t* counters, oda_stream stream);
+
 /* The access sets of the picx.dev summary, section "Local-First Decoding"
  * (S^L_t = {1..min(s,t)} U {max(1,t-w+1)..t}, S^F_t = {1..t}; focus and
  * sliding variants as for oda_decode_full_gated): the positions layer `layer`

@@ -199,3 +199,29 @@ def test_empty_batch_is_a_no_op(lib):
     assert ws > 0
     assert lib.oda_step(ctypes.byref(d), ctypes.byref(kv), 0, FAKE, None, FAKE, FAKE, FAKE, 0.0, FAKE, None,
                         None, None, None, None, FAKE, ws, None) == 0
+
+
+def test_step_static_rejects_bad_arguments_before_any_launch(lib):
+    """The entry point without a workspace validates like oda_step and refuses
+    dims whose workspace exceeds its static scratch, all on the host."""
+    d, kv = _dims(), _kv()
+    s = lib.oda_step_static
+    args = lambda **o: [o.get(k, v) for k, v in (("q", FAKE), ("qf", None), ("k", FAKE), ("v", FAKE),
+                                                 ("sc", FAKE), ("th", 0.0), ("out", FAKE))]
+    call = lambda dims, batch, **o: s(ctypes.byref(dims), ctypes.byref(kv), batch, *args(**o), None, None,
+                                      None, None, None, None)
+    assert call(d, 1, q=None) == -1
+    assert call(d, 1, sc=None) == -1
+    assert call(d, 1, out=None) == -1
+    assert call(d, 1, th=float("nan")) == -1
+    assert call(d, 1, qf=FAKE + 8) == -1
+    assert call(d, 4) == -1                                  # batch > max_batch
+    assert call(_dims(head_dim=96), 1) == -2                 # not built
+    assert call(d, 0) == 0                                   # empty batch: nothing launched
+    # a workspace above the 4 MiB of static scratch is refused
+    big = _dims(max_batch=4096, max_blocks_per_seq=8192, num_q_heads=64, num_kv_heads=8)
+    assert lib.oda_workspace_size(ctypes.byref(big), 4096) > 4 << 20
+    assert call(big, 4096) == -4
+    kv2 = _kv()
+    kv2.k_ring = None
+    assert s(ctypes.byref(d), ctypes.byref(kv2), 1, *args(), None, None, None, None, None, None) == -1
