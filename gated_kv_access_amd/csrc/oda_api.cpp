@@ -150,7 +150,8 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
   w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
   w.claim_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
-  w.commit_ticket_off = up(w.claim_off + sizeof(int32_t) * (size_t)b * p.Hkv);
+  // one tail-pool counter per (request, KV head), each on its own 256-byte line
+  w.commit_ticket_off = up(w.claim_off + sizeof(int32_t) * oda::kCounterStride * (size_t)b * p.Hkv);
   w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
   w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
   const size_t ml_copies = p.D >= 64 ? (size_t)p.D / 64 : 1;  // one (m, l) per merging wave

@@ -13,6 +13,9 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 8;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
 constexpr size_t kWsHeader = 256;  // error word, call count, spare
+// Device-scope atomics on words that share a cache line are served one after
+// another: counters that many workgroups add to sit this many words apart.
+constexpr int32_t kCounterStride = 64;
 
 // Attention passes read their rows either from a ring (Local passes and all
 // passes of sliding layers) or from the paged cache (Full / focus passes).
@@ -92,7 +95,7 @@ struct AttnParams {
   float* part_o;              // [batch][Hq][splits][d]
   float* part_ml;             // [batch][Hq][splits][d / 64][2]  (one copy per merging wave)
   int32_t* tickets;           // [batch][Hkv], zero between launches
-  int32_t* claims;            // [batch][Hkv], zero between launches: pool tiles taken (paged passes)
+  int32_t* claims;            // [batch][Hkv] x kCounterStride, zero between launches: pool tiles taken
   int32_t merge_mode;         // MergeMode
   uint32_t* err;
   float scale_log2;           // softmax scale * k_scale * log2(e)

@@ -403,6 +403,10 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
 // dispatched last and merges, takes the fewest rows.  The first `used` ranges
 // are non-empty; `split` < `used` gets [begin, end).
 constexpr int32_t kSplitRowUnit = 16;
+// Tail-pool tiles per split (paged passes over long ranges).  With its
+// counter alone on a cache line, a third tile per split shortens the bf16
+// Full pass at 128K by about 1 us; a fourth gains nothing more.
+constexpr int32_t kPoolTilesPerSplit = 3;
 __device__ __forceinline__ void split_rows(int32_t n, int32_t splits, int32_t split, int32_t& used,
                                            int32_t& begin, int32_t& end) {
   const int32_t units = (n + kSplitRowUnit - 1) / kSplitRowUnit;
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   int32_t spec_blk[NP];
   int32_t spec_S = 0;
   if constexpr (SRC == kSrcPaged) {
-    const int32_t pool_rows = 2 * P.splits * TILE;
+    const int32_t pool_rows = kPoolTilesPerSplit * P.splits * TILE;
     const int32_t S = ((P.capacity - pool_rows) / P.splits) & ~(kSplitRowUnit - 1);
     if (!P.rows.focus && P.claims != nullptr && S >= TILE && P.capacity >= 8 * pool_rows) {
       spec_S = S;
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     row_end = row_begin + spec_S;
   } else {
     if constexpr (SRC == kSrcPaged) {
-      const int32_t pool_rows = 2 * P.splits * TILE;
+      const int32_t pool_rows = kPoolTilesPerSplit * P.splits * TILE;
       if (P.claims != nullptr && n_all >= 8 * pool_rows) n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
     }
     split_rows(n_static, P.splits, split, used, row_begin, row_end);
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
             atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
             ok = false;
           } else {
-            off = ((((int64_t)blk * P.Hkv + g) << P.block_shift) + (r0 & bmask)) * D * ES;
+            off = ((((int64_t)g * P.num_blocks + blk) << P.block_shift) + (r0 & bmask)) * D * ES;
           }
         }
       }
@@ -1075,7 +1079,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   if (n_static < n_all) {
     // Pool tile c covers rows n_static + c * TILE .. (the last one ends at n_all).
     const int32_t pool_tiles = (n_all - n_static + TILE - 1) / TILE;
-    int32_t* claim = P.claims + (int64_t)b * P.Hkv + g;
+    int32_t* claim = P.claims + ((int64_t)b * P.Hkv + g) * kCounterStride;
     // Thread 0 takes the next tile index; every wave reads it after a barrier.
     auto take = [&]() {
       if (threadIdx.x == 0) s_claim = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1261,7 +1265,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0]);
     // every split has published, so none claims pool tiles any more
     if (threadIdx.x == 0 && n_static < n_all)
-      __hip_atomic_store(P.claims + (int64_t)b * P.Hkv + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.claims + ((int64_t)b * P.Hkv + g) * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   // Ticket mode: every wave waits until its device-scope partial stores have
@@ -1279,7 +1283,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   merge_and_write<DT, D, G>(P, b, g, used, false, nullptr, nullptr);
   if (threadIdx.x == 0) {  // every ticket (and pool tile) of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n_static < n_all) __hip_atomic_store(P.claims + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n_static < n_all) __hip_atomic_store(P.claims + pair * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1436,7 +1440,7 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams P) {
     const uint4 kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k_new) + src);
     const uint4 vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v_new) + src);
     if (gated) {
-      const int64_t coff = ((((rank * P.num_blocks + blk) * P.Hkv + h) << P.block_shift) + in_blk) * row_bytes + vi * 16;
+      const int64_t coff = ((((rank * P.Hkv + h) * P.num_blocks + blk) << P.block_shift) + in_blk) * row_bytes + vi * 16;
       *reinterpret_cast<uint4*>(static_cast<char*>(P.k_cache) + coff) = kx;
       *reinterpret_cast<uint4*>(static_cast<char*>(P.v_cache) + coff) = vx;
       const int64_t roff = (((rank * P.ring_batch + b) * P.Hkv + h) * P.ring_slots + gslot) * row_bytes + vi * 16;
@@ -1506,7 +1510,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     const int32_t r0 = p - 1;
     const int32_t blk = btab[r0 >> P.block_shift];
     ok = blk >= 0 && (int64_t)blk < P.num_blocks;
-    return (((((int64_t)P.rank * P.num_blocks + blk) * P.Hkv + h) << P.block_shift) + (r0 & bmask)) * row_bytes + vi * 16;
+    return (((((int64_t)P.rank * P.Hkv + h) * P.num_blocks + blk) << P.block_shift) + (r0 & bmask)) * row_bytes + vi * 16;
   };
   auto src_off = [&](int32_t p, int32_t h, int32_t vi) -> int64_t {
     return ((((int64_t)b * P.src_rows + (p - 1)) * P.Hkv + h) * row_bytes) + vi * 16;

@@ -80,13 +80,13 @@ class DecodeState:
         # pass over the host link); the rings stay in HBM.
         self.host_cache = host_cache
         if Lg and host_cache:
-            shape = (Lg, nblocks, Hkv, wl.block_size, d)
+            shape = (Lg, Hkv, nblocks, wl.block_size, d)
             self.k_cache = torch.empty(shape, dtype=dt, pin_memory=True)
             self.v_cache = torch.empty(shape, dtype=dt, pin_memory=True)
             _raw(self.k_cache).view(-1).fill_(_raw_fill(fill, dt))
             _raw(self.v_cache).view(-1).fill_(_raw_fill(fill, dt))
         else:
-            self.k_cache = torch.full((Lg, nblocks, Hkv, wl.block_size, d), fill, dtype=dt, device=self.device) if Lg else None
+            self.k_cache = torch.full((Lg, Hkv, nblocks, wl.block_size, d), fill, dtype=dt, device=self.device) if Lg else None
             self.v_cache = torch.full_like(self.k_cache, fill) if Lg else None
         self.k_ring = torch.full((Lg, Bn, Hkv, R, d), fill, dtype=dt, device=self.device) if Lg else None
         self.v_ring = torch.full_like(self.k_ring, fill) if Lg else None

@@ -121,7 +121,7 @@ typedef struct {
 /* Let Lg / Ls be the numbers of gated / sliding layers.  A layer's cache index
  * is its rank among the layers of its kind.  All arrays are dense, row-major. */
 typedef struct {
-  void* k_cache;               /* [Lg][num_blocks][Hkv][block_size][d]  paged history   */
+  void* k_cache;               /* [Lg][Hkv][num_blocks][block_size][d]  paged history   */
   void* v_cache;               /*   (position p of request b: block block_table[b][(p-1)/bs],
                                      row (p-1) % bs)                                     */
   void* k_ring;                /* [Lg][max_batch][Hkv][s+w][d]  Local ring workspace     */

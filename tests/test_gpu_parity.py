@@ -229,8 +229,8 @@ def test_commit_writes_paged_cache_and_ring_bit_exact():
             for p in range(1, t_end + 1):
                 blk = bt[b, (p - 1) // wl.block_size]
                 row = (p - 1) % wl.block_size
-                assert torch.equal(st.k_cache[layer, blk, :, row], k_all[p - 1])
-                assert torch.equal(st.v_cache[layer, blk, :, row], v_all[p - 1])
+                assert torch.equal(st.k_cache[layer, :, blk, row], k_all[p - 1])
+                assert torch.equal(st.v_cache[layer, :, blk, row], v_all[p - 1])
             for j in range(wl.sink + wl.window):
                 p = int(st.ring_pos[b, j].item())
                 if p:
