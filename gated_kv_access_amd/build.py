@@ -30,19 +30,28 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, extra_hip_flags=()) -> str:
+PHASES_LIB = os.path.join(PKG, "liboda_phases.so")
+
+
+def build(verbose: bool = False, extra_hip_flags=(), phases: bool = False) -> str:
+    """Builds liboda.so, or with phases=True the profiling build
+    liboda_phases.so (the same library with phase stamps, include/oda_phases.h)."""
     os.makedirs(BUILD, exist_ok=True)
-    api_o = os.path.join(BUILD, "oda_api.o")
-    ker_o = os.path.join(BUILD, "oda_kernels.o")
+    tag = "_phases" if phases else ""
+    flags = ["-DODA_PHASE_STAMPS"] if phases else []
+    api_o = os.path.join(BUILD, f"oda_api{tag}.o")
+    ker_o = os.path.join(BUILD, f"oda_kernels{tag}.o")
+    lib = PHASES_LIB if phases else LIB
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "oda_api.cpp"), "-o", api_o], verbose)
-    _run([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-c", os.path.join(CSRC, "oda_kernels.hip"), "-o", ker_o],
+    _run([HIPCC, *HIP_FLAGS, *flags, *extra_hip_flags, "-c", os.path.join(CSRC, "oda_kernels.hip"), "-o", ker_o],
          verbose)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, phases=True)
     sys.exit(0)

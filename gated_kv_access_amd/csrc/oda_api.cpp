@@ -147,7 +147,8 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.err_off = 0;
   w.count_off = 4;
   w.list_off = oda::kWsHeader;
-  w.len_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.order_off = up(w.list_off + sizeof(int32_t) * (size_t)b);
+  w.len_off = up(w.order_off + sizeof(int32_t) * (size_t)b);
   w.ticket_off = up(w.len_off + sizeof(int32_t) * (size_t)b);
   w.claim_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
   // one tail-pool counter per (request, KV head), each on its own 256-byte line
@@ -330,15 +331,17 @@ oda_status run_step(const Ctx& c, const oda_kv* kv, int32_t batch, const void* q
   // 3) Gate: compaction of the fired requests, counters.
   int32_t* list = call_list ? call_list : reinterpret_cast<int32_t*>(c.base + c.ws.list_off);
   int32_t* count = call_count ? call_count : reinterpret_cast<int32_t*>(c.base + c.ws.count_off);
+  int32_t* order = reinterpret_cast<int32_t*>(c.base + c.ws.order_off);
   int32_t* lens = reinterpret_cast<int32_t*>(c.base + c.ws.len_off);
-  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, lens, full_calls, counters,
+  int rc = oda::launch_gate(p, *kv, batch, recall_score, theta, list, count, order, lens, full_calls, counters,
                             stream);
   if (rc) return ODA_ERR_HIP;
-  // 4) Full recomputation of every layer for the fired requests.
+  // 4) Full recomputation of every layer for the fired requests, dispatched
+  //    longest first.
   for (int32_t l = 0; l < p.L; ++l) {
     st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
                   at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  list, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
+                  order, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
     if (st != ODA_OK) return st;
   }
   // 5) Fused commit of position t for all layers.
@@ -441,7 +444,7 @@ oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch, const
   if (!recall_score || isnan(theta) || !kv || !kv->seq_len) return ODA_ERR_INVALID_ARG;
   if (c.plan.focus && c.plan.Lg > 0 && counters && !kv->focus_range) return ODA_ERR_INVALID_ARG;
   return hip_status(oda::launch_gate(c.plan, *kv, batch, recall_score, theta, call_list, call_count,
-                                     nullptr, full_calls, counters, stream));
+                                     nullptr, nullptr, full_calls, counters, stream));
 }
 
 oda_status oda_step(const oda_dims* dims, const oda_kv* kv, int32_t batch, const void* q_local,

@@ -39,7 +39,7 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, len_off, ticket_off, claim_off, commit_ticket_off, part_o_off, part_ml_off,
+  size_t err_off, count_off, list_off, order_off, len_off, ticket_off, claim_off, commit_ticket_off, part_o_off, part_ml_off,
       total;
   int32_t max_splits;
 };
@@ -81,7 +81,7 @@ struct AttnParams {
   const int32_t* seq_len;
   const int32_t* call_list;   // kGateList
   const int32_t* call_count;
-  const int32_t* call_len;    // kGateList: committed length of each listed request
+  const int32_t* call_len;    // kGateList: committed length of each listed request (same order as call_list)
   const int64_t* focus_range;
   const float* score;         // kGateBallot
   float theta;
@@ -104,9 +104,12 @@ struct AttnParams {
 
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
+// call_list (ascending; needed when disp_list is given) and call_count are the
+// compacted decisions; disp_list / disp_len (nullable) the fired requests and
+// their committed lengths in the Full passes' dispatch order (longest first).
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
-                int32_t* call_list, int32_t* call_count, int32_t* call_len, int64_t* full_calls,
-                int64_t* counters, oda_stream s);
+                int32_t* call_list, int32_t* call_count, int32_t* disp_list, int32_t* disp_len,
+                int64_t* full_calls, int64_t* counters, oda_stream s);
 int launch_commit(const Plan& p, const oda_kv& kv, int32_t batch, const void* k_new,
                   const void* v_new, int32_t* tickets, uint32_t* err, oda_stream s);
 int launch_prefill(const Plan& p, const oda_kv& kv, int32_t batch, int32_t layer,

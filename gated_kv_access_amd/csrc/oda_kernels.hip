@@ -37,6 +37,45 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Phase stamps of the profiling build (compiled with ODA_PHASE_STAMPS into
+// liboda_phases.so, include/oda_phases.h; the product library has none):
+// thread 0 of every attention workgroup records the chip's 100 MHz real-time
+// counter at eight points of its work -- entry, request state known, first
+// tile reduced, static rows done, tail pool done, fold barrier passed, partial
+// stored, merge done -- and the XCD it ran on.  Slots are indexed by the
+// workgroup's linear id; a launch overwrites what an earlier one left.
+constexpr int kPhaseGroups = 65536;
+constexpr int kPhases = 8;
+#ifdef ODA_PHASE_STAMPS
+__device__ unsigned long long g_phase_stamps[kPhaseGroups * kPhases];
+__device__ unsigned g_phase_xcc[kPhaseGroups];
+__device__ __forceinline__ int phase_slot() {
+  return (int)((((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) % kPhaseGroups);
+}
+#define ODA_PHASE(k)                                                                    \
+  do {                                                                                  \
+    if (threadIdx.x == 0) g_phase_stamps[phase_slot() * kPhases + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+// A stamp taken once this wave's stores have completed.
+#define ODA_PHASE_STORED(k)                          \
+  do {                                               \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); \
+    ODA_PHASE(k);                                    \
+  } while (0)
+#define ODA_PHASE_XCC()                                                            \
+  do {                                                                             \
+    if (threadIdx.x == 0) {                                                        \
+      unsigned x;                                                                  \
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));             \
+      g_phase_xcc[phase_slot()] = x & 15u;                                          \
+    }                                                                              \
+  } while (0)
+#else
+#define ODA_PHASE(k) ((void)0)
+#define ODA_PHASE_STORED(k) ((void)0)
+#define ODA_PHASE_XCC() ((void)0)
+#endif
+
 // ----------------------------------------------------------------------------
 // lane exchange
 
@@ -594,6 +633,8 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
   constexpr int TILE = Gm::TILE;
   constexpr int ES = Gm::ES, QES = Gm::QES;
+  ODA_PHASE(0);
+  ODA_PHASE_XCC();
 
   // Paged Full passes with the tail pool, no focus region: when the context
   // fills the block table to within the pool and the workgroup's request
@@ -655,6 +696,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   } else {
     if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
+    ODA_PHASE(1);
     t = committed + 1;
     if (t - 1 > P.capacity) {
       if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_CAPACITY);
@@ -1063,6 +1105,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   if constexpr (SRC == kSrcRing) {
     if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
+    ODA_PHASE(1);
     t = committed + 1;
     rst = ring_state(t, P.rows.sink, P.rows.window);
   }
@@ -1071,10 +1114,12 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     resolve_blocks(tile + 2, ba);
     if (has_b) load_tile(tile + 1, bb, rb);
     process_tile(ra);
+    if (tile == 0) ODA_PHASE(2);
     resolve_blocks(tile + 3, bb);
     if (tile + 2 < n_tiles) load_tile(tile + 2, ba, ra);
     if (has_b) process_tile(rb);
   }
+  ODA_PHASE(3);
   __shared__ int32_t s_claim;
   if (n_static < n_all) {
     // Pool tile c covers rows n_static + c * TILE .. (the last one ends at n_all).
@@ -1115,6 +1160,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
   }
 
+  ODA_PHASE(4);
   constexpr int FOLD_ROWS = kWavesPerGroup;  // rows of the LDS fold: one per wave
   __shared__ float s_wmax[kWavesPerGroup][G];
   constexpr int RS = G * D + 4;  // LDS row stride (words)
@@ -1230,6 +1276,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
     }
     __syncthreads();
+    ODA_PHASE(5);
     for (int idx = threadIdx.x; idx < G * D * TPO; idx += kGroupThreads) {
       const int out_i = idx / TPO, part = idx % TPO;
       const int h = out_i / D, e = out_i % D;
@@ -1260,9 +1307,14 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
 
   if (poll) {
-    if (!merges_here) return;
+    if (!merges_here) {
+      ODA_PHASE_STORED(6);
+      return;
+    }
     __syncthreads();
+    ODA_PHASE(6);
     merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0]);
+    ODA_PHASE_STORED(7);
     // every split has published, so none claims pool tiles any more
     if (threadIdx.x == 0 && n_static < n_all)
       __hip_atomic_store(P.claims + ((int64_t)b * P.Hkv + g) * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1274,6 +1326,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   const int64_t pair = (int64_t)b * P.Hkv + g;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  ODA_PHASE(6);
   if (threadIdx.x == 0) {
     const int32_t prev = __hip_atomic_fetch_add(&P.tickets[pair], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == used - 1;
@@ -1281,6 +1334,7 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   __syncthreads();
   if (!s_last) return;
   merge_and_write<DT, D, G>(P, b, g, used, false, nullptr, nullptr);
+  ODA_PHASE_STORED(7);
   if (threadIdx.x == 0) {  // every ticket (and pool tile) of this launch is taken: ready for the next launch
     __hip_atomic_store(&P.tickets[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n_static < n_all) __hip_atomic_store(P.claims + pair * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1300,7 +1354,8 @@ struct GateParams {
   const int64_t* focus_range;
   int32_t* call_list;
   int32_t* call_count;
-  int32_t* call_len;  // optional: committed length of each listed request
+  int32_t* disp_list;  // optional: the fired requests in dispatch order (longest first)
+  int32_t* disp_len;   // their committed lengths, in the same order
   int64_t* full_calls;
   int64_t* counters;
 };
@@ -1315,9 +1370,14 @@ __device__ int64_t focus_set_size(int32_t t, int32_t s, int32_t w, int64_t fa, i
   return (int64_t)paged_intervals(rs, t, fa, fb).total + 1;
 }
 
+// Fired requests up to this many are put in dispatch order by length (more
+// keep the list's order).
+constexpr int32_t kSortMax = 1024;
+
 __global__ __launch_bounds__(1024) void gate_kernel(GateParams P) {
   __shared__ int32_t s_wave_count[1024 / kWave];
   __shared__ int32_t s_base;
+  __shared__ int32_t s_fid[ODA_MAX_BATCH], s_flen[ODA_MAX_BATCH];  // fired requests by list position
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   if (threadIdx.x == 0) s_base = 0;
@@ -1360,8 +1420,12 @@ __global__ __launch_bounds__(1024) void gate_kernel(GateParams P) {
     int32_t before = s_base;
     for (int w = 0; w < wave; ++w) before += s_wave_count[w];
     const uint64_t lower = lane == 0 ? 0ull : (ballot & ((1ull << lane) - 1ull));
-    if (fire && P.call_list) P.call_list[before + __popcll(lower)] = b;
-    if (fire && P.call_len) P.call_len[before + __popcll(lower)] = t - 1;
+    const int32_t at = before + __popcll(lower);
+    if (fire && P.call_list) P.call_list[at] = b;
+    if (fire) {
+      s_fid[at] = b;
+      s_flen[at] = t - 1;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
       int32_t total = 0;
@@ -1374,6 +1438,28 @@ __global__ __launch_bounds__(1024) void gate_kernel(GateParams P) {
   if (P.call_list)
     for (int32_t i = count + threadIdx.x; i < P.batch; i += blockDim.x) P.call_list[i] = -1;
   if (threadIdx.x == 0 && P.call_count) *P.call_count = count;
+  // Dispatch order of the Full passes: the longest request first (ties by
+  // request id), so that when one launch takes several rounds of workgroups
+  // the last to be dispatched are the shortest.  Slot i of the list goes to
+  // rank i's place: the number of fired requests that come before it.
+  if (P.disp_list == nullptr) return;
+  if (count > kSortMax) {
+    for (int32_t i = threadIdx.x; i < count; i += blockDim.x) {
+      P.disp_list[i] = s_fid[i];
+      P.disp_len[i] = s_flen[i];
+    }
+    return;
+  }
+  for (int32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    const int32_t li = s_flen[i];
+    int32_t rank = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const int32_t lj = s_flen[j];
+      rank += (lj > li) || (lj == li && j < i);
+    }
+    P.disp_list[rank] = s_fid[i];
+    P.disp_len[rank] = li;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1765,8 +1851,8 @@ int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stre
 }
 
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,
-                int32_t* call_list, int32_t* call_count, int32_t* call_len, int64_t* full_calls,
-                int64_t* counters, oda_stream s) {
+                int32_t* call_list, int32_t* call_count, int32_t* disp_list, int32_t* disp_len,
+                int64_t* full_calls, int64_t* counters, oda_stream s) {
   if (batch <= 0) return 0;
   GateParams g{};
   g.batch = batch;
@@ -1788,7 +1874,8 @@ int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* sco
   g.focus_range = kv.focus_range;
   g.call_list = call_list;
   g.call_count = call_count;
-  g.call_len = call_len;
+  g.disp_list = disp_list;
+  g.disp_len = disp_len;
   g.full_calls = full_calls;
   g.counters = counters;
   const int threads = batch >= 1024 ? 1024 : ((batch + 63) / 64) * 64;
@@ -2197,3 +2284,21 @@ int host_device_pointer(void* host_ptr, void** device_ptr) {
 }
 
 }  // namespace oda
+
+#ifdef ODA_PHASE_STAMPS
+extern "C" int oda_phase_stamps_read(unsigned long long* stamps, unsigned* xcc, size_t groups) {
+  if (groups > (size_t)oda::kPhaseGroups || !stamps || !xcc) return (int)hipErrorInvalidValue;
+  hipError_t e = hipMemcpyFromSymbol(stamps, HIP_SYMBOL(oda::g_phase_stamps),
+                                     groups * oda::kPhases * sizeof(unsigned long long), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemcpyFromSymbol(xcc, HIP_SYMBOL(oda::g_phase_xcc), groups * sizeof(unsigned), 0,
+                                  hipMemcpyDeviceToHost);
+}
+
+extern "C" int oda_phase_stamps_clear(void) {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(oda::g_phase_stamps));
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemset(p, 0, sizeof(unsigned long long) * oda::kPhaseGroups * oda::kPhases);
+}
+#endif

@@ -225,3 +225,21 @@ def test_step_static_rejects_bad_arguments_before_any_launch(lib):
     kv2 = _kv()
     kv2.k_ring = None
     assert s(ctypes.byref(d), ctypes.byref(kv2), 1, *args(), None, None, None, None, None, None) == -1
+
+
+def test_profiling_build_exports_the_phase_calls():
+    """liboda_phases.so (the profiling build) exports what include/oda_phases.h
+    declares on top of every oda.h symbol; the product library exports none of it."""
+    from gated_kv_access_amd.build import PHASES_LIB
+    if not os.path.exists(PHASES_LIB):
+        from gated_kv_access_amd import build
+        build.build(phases=True)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "oda_phases.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(oda_[a-z_]+)\s*\(", text)))
+    assert declared == ["oda_phase_stamps_clear", "oda_phase_stamps_read"]
+    prof = ctypes.CDLL(PHASES_LIB)
+    for name in declared + _declared():
+        assert hasattr(prof, name), name
+    product = ctypes.CDLL(B.LIB_PATH)
+    for name in declared:
+        assert not hasattr(product, name), name
