@@ -371,9 +371,10 @@ def recall_head_leg(head, hx, batch, launches=50):
 
 def roofline_leg(args, st, wl, q, k_new, v_new):
     """The dominant kernel: the Full-pass attention kernel (split-K over the paged
-    cache + last-workgroup merge), one launch per oda_decode_full_gated call on a
-    gated layer, every request firing.  Timed over all its launches with HIP
-    events on the stream the launches go to (torch's current stream)."""
+    cache + merge), one launch per oda_decode_full_gated call on a gated layer,
+    every request firing.  The launches are captured into a HIP graph and
+    replayed, as in the decode step, and timed over one replay with HIP events
+    on the stream the graph replays on (torch's current stream)."""
     import torch
 
     from gated_kv_access_amd import binding as B
@@ -395,16 +396,22 @@ def roofline_leg(args, st, wl, q, k_new, v_new):
     ks = [k_new[-1, l].contiguous() for l in gated]
     vs = [v_new[-1, l].contiguous() for l in gated]
     R = args.roofline_launches
-    for i in range(len(gated)):
-        B.decode_full_gated(st.dims, st.kv, gated[i], Bn, qs[i], ks[i], vs[i], fire, 0.0, out, None, None, None,
-                            st.workspace)
+    # The launches are replayed from a HIP graph, as the decode step runs them.
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(R):
+                j = i % len(gated)
+                B.decode_full_gated(st.dims, st.kv, gated[j], Bn, qs[j], ks[j], vs[j], fire, 0.0, out, None, None,
+                                    None, st.workspace)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for i in range(R):
-        j = i % len(gated)
-        B.decode_full_gated(st.dims, st.kv, gated[j], Bn, qs[j], ks[j], vs[j], fire, 0.0, out, None, None, None,
-                            st.workspace)
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
     avg_us = e0.elapsed_time(e1) * 1e3 / R
