@@ -231,6 +231,21 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a K/V row.  STREAM: the load carries the non-temporal hint.
+// K/V rows are read once per pass; with the hint, loads whose instruction
+// covers whole 128-byte lines stream about 14% faster (6.6 vs 5.7 TB/s for
+// shuffled 4 KiB blocks), while half-line loads gain nothing or lose a little.
+template <bool STREAM>
+__device__ __forceinline__ uint4 kv_load(const char* p) {
+  if constexpr (STREAM) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -282,14 +297,23 @@ struct Geo {
   static constexpr bool WIDE = SRC == kSrcRing && DT != ODA_F32 && ROW_BYTES <= 16 * 16 && !MF;
   static constexpr int NARROW = WIDE || MF ? 1 : (G >= 8 ? 4 : (G >= 4 ? 2 : 1));  // divides NV
   static constexpr int PASSES = WIDE || MF ? 1 : (G >= 4 ? 2 : 1);                  // multiplies NP
-  static constexpr int NV = WIDE ? 1 : MF ? D * ES / 64 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;  // 16-byte K/V vectors per lane per row
+  static constexpr int NV0 = WIDE ? 1 : MF ? D * ES / 64 : (DT == ODA_FP8_E4M3 ? 2 : 4) / NARROW;
+  // Paged bf16 / f32 passes read whole 128-byte lines of a row per load
+  // instruction (at least 8 lanes per row), with the non-temporal hint: loads
+  // that cover half lines of twice as many rows stream about 12% slower and
+  // gain nothing from the hint.  Fewer vectors per lane, more passes.  (FP8
+  // rows would need a single vector per lane and four passes per tile, whose
+  // per-row work costs more than the loads gain.)
+  static constexpr int LINE_NV = ROW_BYTES >= 256 ? ROW_BYTES / 128 : 1;
+  static constexpr int NV = SRC == kSrcPaged && !MF && ES >= 2 && NV0 > LINE_NV ? LINE_NV : NV0;  // 16-byte K/V vectors per lane per row
   static constexpr int LPR = ROW_BYTES / (16 * NV);  // lanes sharing a row
   static constexpr int RPP = kWave / LPR;            // rows per wave pass
   static constexpr int EPV = 16 / ES;                // elements per 16-byte K/V vector
   static constexpr int EPL = NV * EPV;               // elements per lane per row
   static constexpr int QV = EPL * QES / 16;          // 16-byte query vectors per lane per head
   static constexpr int QPV = QV / NV;                // query vectors per K/V vector
-  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP) : (DT == ODA_FP8_E4M3 ? 2 : 1) * (MF ? 1 : PASSES);  // passes per tile
+  static constexpr int NP = WIDE ? 128 / (kWavesPerGroup * RPP)
+                                : (DT == ODA_FP8_E4M3 ? 2 : 1) * (MF ? 1 : PASSES) * (NV0 / NV);  // passes per tile
   static constexpr int TILE = kWavesPerGroup * NP * RPP;
   static_assert(LPR >= 2 && LPR <= 16, "row must span 2..16 lanes");
   static_assert(QV % NV == 0 && NP >= 1, "whole query vectors per K/V vector");
@@ -442,10 +466,27 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
 // dispatched last and merges, takes the fewest rows.  The first `used` ranges
 // are non-empty; `split` < `used` gets [begin, end).
 constexpr int32_t kSplitRowUnit = 16;
-// Tail-pool tiles per split (paged passes over long ranges).  With its
-// counter alone on a cache line, a third tile per split shortens the bf16
-// Full pass at 128K by about 1 us; a fourth gains nothing more.
-constexpr int32_t kPoolTilesPerSplit = 3;
+// Tail-pool rows per split (paged passes over long ranges), rounded down to
+// whole tiles: 3 bf16 tiles.  Pools of 6, 10 and 16 tiles per split measured
+// no faster at 128K.
+constexpr int32_t kPoolRowsPerSplit = 384;
+// The pool's block ids are staged in LDS when the pool starts; the pool is
+// sized so that they fit.
+constexpr int32_t kPoolBlkMax = 2048;
+// Rows of the tail pool of a paged pass (0: none).  Its rows, plus what the
+// whole-unit rounding of the static shares leaves over (under
+// kSplitRowUnit rows per split), span at most kPoolBlkMax blocks.
+__device__ __forceinline__ int32_t pool_rows_of(int32_t splits, int32_t block_shift, int32_t tile) {
+  const int64_t cap = ((int64_t)(kPoolBlkMax - 2) << block_shift) - (int64_t)kSplitRowUnit * splits;
+  int64_t rows = (int64_t)kPoolRowsPerSplit * splits / tile * tile;
+  if (rows > cap) rows = cap / tile * tile;
+  return rows >= tile ? (int32_t)rows : 0;
+}
+// Takes the next pool tile: a relaxed device-scope increment of the counter.
+__device__ __forceinline__ int32_t claim_next(int32_t* counter) {
+  return (int32_t)__builtin_amdgcn_atomic_inc32(reinterpret_cast<uint32_t*>(counter), 0xFFFFFFFFu, __ATOMIC_RELAXED,
+                                                "agent");
+}
 __device__ __forceinline__ void split_rows(int32_t n, int32_t splits, int32_t split, int32_t& used,
                                            int32_t& begin, int32_t& end) {
   const int32_t units = (n + kSplitRowUnit - 1) / kSplitRowUnit;
@@ -488,7 +529,7 @@ __device__ __forceinline__ int32_t ballot_request(const AttnParams& P, int32_t s
 }
 
 // Writes the compacted list of fired requests (ascending, then -1) and its length.
-__device__ void write_call_list(const AttnParams& P) {
+__device__ __forceinline__ void write_call_list(const AttnParams& P) {
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
   int32_t seen = 0;
@@ -535,7 +576,7 @@ constexpr int kMergeBatch = 32;  // partials loaded per round by one output thre
 // next launch as soon as they are read.  Returns false (and sets ODA_DEVERR_MERGE_WAIT) if polling gives up.
 // No LDS writes, no barrier.
 template <int DT, int D, int G>
-__device__ bool merge_output(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
+__device__ __forceinline__ bool merge_output(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
                              const float* own_o, const float* own_ml, int tid) {
   const int lane = tid & (kWave - 1);
   const int h = tid / D, e = tid % D;
@@ -611,7 +652,7 @@ __device__ bool merge_output(const AttnParams& P, int32_t b, int32_t g, int32_t 
 }
 
 template <int DT, int D, int G>
-__device__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
+__device__ __forceinline__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
                                 const float* own_o, const float* own_ml) {
   static_assert(D % kWave == 0, "one head per wave");
   for (int tid = threadIdx.x; tid < G * D; tid += kGroupThreads)
@@ -645,9 +686,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   int32_t spec_blk[NP];
   int32_t spec_S = 0;
   if constexpr (SRC == kSrcPaged) {
-    const int32_t pool_rows = kPoolTilesPerSplit * P.splits * TILE;
+    const int32_t pool_rows = pool_rows_of(P.splits, P.block_shift, TILE);
     const int32_t S = ((P.capacity - pool_rows) / P.splits) & ~(kSplitRowUnit - 1);
-    if (!P.rows.focus && P.claims != nullptr && S >= TILE && P.capacity >= 8 * pool_rows) {
+    if (!P.rows.focus && P.claims != nullptr && pool_rows > 0 && S >= TILE && P.capacity >= 2 * pool_rows) {
       spec_S = S;
       const int32_t* bt = P.block_table + (int64_t)blockIdx.z * P.max_blocks;
       const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -713,10 +754,11 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   // Row n_rows is the current token t, read from k_cur / v_cur: it is
   // processed like any other row, by the last split (or, with the pool, by the
   // workgroup that takes the last pool tile).
-  // Paged passes over long ranges keep a pool of tail tiles, 2 per split, at
-  // the end of the range: the splits divide rows [0, n_static) statically and
-  // then take pool tiles one at a time from a per-(request, KV head) counter,
-  // so workgroups that stream faster than others take more of the tail.
+  // Paged passes over long ranges (no focus region) keep a pool of tail
+  // tiles, kPoolTilesPerSplit per split, at the end of the range: the splits
+  // divide rows [0, n_static) statically and then take pool tiles from a
+  // per-(request, KV head) counter, so workgroups that stream faster than
+  // others take more of the tail.
   const int32_t n_all = n_rows + 1;
   int32_t n_static = n_all;
   int32_t used, row_begin, row_end;
@@ -728,8 +770,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     row_end = row_begin + spec_S;
   } else {
     if constexpr (SRC == kSrcPaged) {
-      const int32_t pool_rows = kPoolTilesPerSplit * P.splits * TILE;
-      if (P.claims != nullptr && n_all >= 8 * pool_rows) n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
+      const int32_t pool_rows = pool_rows_of(P.splits, P.block_shift, TILE);
+      if (!P.rows.focus && P.claims != nullptr && pool_rows > 0 && n_all >= 2 * pool_rows)
+        n_static = (n_all - pool_rows) & ~(kSplitRowUnit - 1);
     }
     split_rows(n_static, P.splits, split, used, row_begin, row_end);
     if (split >= used) return;
@@ -867,8 +910,10 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         if (ok) {
-          R.k[i][j] = *reinterpret_cast<const uint4*>(kb + off + (j * LPR + sub) * 16);
-          R.v[i][j] = *reinterpret_cast<const uint4*>(vb + off + (j * LPR + sub) * 16);
+          // non-temporal where a load instruction covers whole 128-byte lines
+          constexpr bool kStream = SRC == kSrcRing || LPR * 16 >= 128;
+          R.k[i][j] = kv_load<kStream>(kb + off + (j * LPR + sub) * 16);
+          R.v[i][j] = kv_load<kStream>(vb + off + (j * LPR + sub) * 16);
         } else {
           R.k[i][j] = make_uint4(0, 0, 0, 0);
           R.v[i][j] = make_uint4(0, 0, 0, 0);
@@ -909,14 +954,16 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
           char* dst = vt + rrow * VST + (j * LPR + sub) * EPV * 2;
+          // a paged row outside the sums may hold anything (pool loads are unconditional)
+          const uint4 vv = SRC == kSrcPaged && !R.valid[i] ? make_uint4(0, 0, 0, 0) : R.v[i][j];
           if constexpr (DT == ODA_FP8_E4M3) {
-            const uint4 w = R.v[i][j];
+            const uint4 w = vv;
             *reinterpret_cast<uint4*>(dst) = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
                                                         fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
             *reinterpret_cast<uint4*>(dst + 16) = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
                                                              fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
           } else {
-            *reinterpret_cast<uint4*>(dst) = R.v[i][j];
+            *reinterpret_cast<uint4*>(dst) = vv;
           }
         }
         wave_lds_exchange();  // the pass's V rows are in LDS before any lane reads them transposed
@@ -1059,7 +1106,9 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
       }
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const uint32_t w4[4] = {R.v[i][j].x, R.v[i][j].y, R.v[i][j].z, R.v[i][j].w};
+        // a paged row outside the sums may hold anything (pool loads are unconditional)
+        const uint4 vv = SRC == kSrcPaged && !R.valid[i] ? make_uint4(0, 0, 0, 0) : R.v[i][j];
+        const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if constexpr (DT == ODA_FP8_E4M3) {
@@ -1092,6 +1141,20 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     }
   };
 
+  // Element by element (an aggregate copy can leave the tiles in scratch memory).
+  auto copy_tile = [&](const TileRegs& from, TileRegs& to) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        to.k[i][j] = from.k[i][j];
+        to.v[i][j] = from.v[i][j];
+      }
+      to.valid[i] = from.valid[i];
+      to.live[i] = from.live[i];
+      to.row[i] = from.row[i];
+    }
+  };
   TileRegs ra, rb;
   BlockIds ba, bb;
   if (spec_hit) {
@@ -1120,44 +1183,123 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
     if (has_b) process_tile(rb);
   }
   ODA_PHASE(3);
-  __shared__ int32_t s_claim;
   if (n_static < n_all) {
-    // Pool tile c covers rows n_static + c * TILE .. (the last one ends at n_all).
-    const int32_t pool_tiles = (n_all - n_static + TILE - 1) / TILE;
+    // Tail pool.  Tile c covers rows n_static + c * TILE .. (the last one ends
+    // at n_all).  One round trip claims the workgroup's first two tiles and
+    // stages the block ids of every pool row in LDS; after that each claim is
+    // issued before the loads of the tile already claimed, so that its result
+    // is waited for together with the tile being reduced and two tiles stay
+    // in flight.  Pool loads are unconditional (rows outside the tile read
+    // the current token's row and are masked when the tile is reduced), which
+    // keeps the wait counts exact.
+    __shared__ int32_t s_claim[2];
+    __shared__ int32_t s_pool_blk[kPoolBlkMax];
+    // (uniform per workgroup; readfirstlane makes the loop's exits scalar branches)
+    const int32_t pool_tiles = __builtin_amdgcn_readfirstlane((n_all - n_static + TILE - 1) / TILE);
     int32_t* claim = P.claims + ((int64_t)b * P.Hkv + g) * kCounterStride;
-    // Thread 0 takes the next tile index; every wave reads it after a barrier.
-    auto take = [&]() {
-      if (threadIdx.x == 0) s_claim = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      const int32_t c = s_claim;
-      __syncthreads();  // read by every wave before the next claim overwrites it
-      return c;
-    };
-    auto select = [&](int32_t c) {
-      row_begin = n_static + c * TILE;
-      row_end = min(row_begin + TILE, n_all);
-    };
-    // One tile ahead: while tile c's K/V loads are in flight the next index is
-    // taken, and its block ids are looked up while tile c is reduced.
-    int32_t c = take();
-    if (c < pool_tiles) {
-      select(c);
-      resolve_blocks(0, ba);
-      for (;;) {
-        load_tile(0, ba, ra);
-        const int32_t next = take();
-        if (next < pool_tiles) {
-          select(next);
-          resolve_blocks(0, bb);
-          select(c);  // the rows of the tile being reduced
-        }
-        process_tile(ra);
-        if (next >= pool_tiles) break;
-        c = next;
-        select(c);
-        ba = bb;
+    // rows n_static .. n_rows - 1 are positions n_static + 1 .. n_rows
+    const int32_t first_blk = n_static >> P.block_shift;
+    const int32_t n_blk = n_rows > n_static ? min(((n_rows - 1) >> P.block_shift) - first_blk + 1, kPoolBlkMax) : 0;
+    {
+      int32_t first = 0;
+      if (threadIdx.x == 0) first = __hip_atomic_fetch_add(claim, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      constexpr int IDS = kPoolBlkMax / kGroupThreads;
+      int32_t ids[IDS];
+#pragma unroll
+      for (int k = 0; k < IDS; ++k) {
+        const int32_t idx = threadIdx.x + k * kGroupThreads;
+        ids[k] = idx < n_blk ? btab[first_blk + idx] : -1;
       }
+#pragma unroll
+      for (int k = 0; k < IDS; ++k) s_pool_blk[threadIdx.x + k * kGroupThreads] = ids[k];
+      if (threadIdx.x == 0) s_claim[0] = first;
+      __syncthreads();
     }
+    uint32_t bad_blk = 0;
+    auto resolve_pool = [&](int32_t c, BlockIds& B) {
+      const int32_t r0 = n_static + c * TILE;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int32_t row = r0 + (i * kWavesPerGroup + wave) * RPP + rrow;
+        const int32_t k = (row >> P.block_shift) - first_blk;
+        B.blk[i] = row < n_rows && k < n_blk ? s_pool_blk[k] : -1;
+      }
+    };
+    auto load_pool = [&](int32_t c, const BlockIds& B, TileRegs& R) {
+      const int32_t r0 = n_static + c * TILE;
+      const int32_t r1 = min(r0 + TILE, n_all);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int32_t pass0 = r0 + (i * kWavesPerGroup + wave) * RPP;
+        const int32_t row = pass0 + rrow;
+        R.row[i] = row;
+        R.live[i] = pass0 < r1;
+        const int32_t blk = B.blk[i];
+        const bool paged = row < r1 && row < n_rows;
+        const bool blk_ok = blk >= 0 && (int64_t)blk < P.num_blocks;
+        bad_blk |= paged && !blk_ok;
+        const bool from_cache = paged && blk_ok;
+        R.valid[i] = from_cache || row == n_rows;
+        const char* kb = from_cache ? kbase : static_cast<const char*>(P.k_cur);
+        const char* vb = from_cache ? vbase : static_cast<const char*>(P.v_cur);
+        const int64_t off =
+            from_cache ? ((((int64_t)g * P.num_blocks + blk) << P.block_shift) + (row & bmask)) * D * ES : cur_off;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          constexpr bool kStream = LPR * 16 >= 128;
+          R.k[i][j] = kv_load<kStream>(kb + off + (j * LPR + sub) * 16);
+          R.v[i][j] = kv_load<kStream>(vb + off + (j * LPR + sub) * 16);
+        }
+      }
+    };
+    // (claims are read from LDS: readfirstlane keeps them, and the branches on
+    // them, scalar)
+    const int32_t c0 = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    int32_t c1 = c0 + 1;
+    int slot = 1;
+    if (c0 < pool_tiles) {
+      resolve_pool(c0, ba);
+      load_pool(c0, ba, ra);
+      // ra holds tile c0 (in flight); c1 is claimed.  Each half of the loop
+      // claims the tile after next, loads the claimed one and reduces the
+      // one in flight.  The last tile is reduced from ra after the loop (one
+      // copy of the reduction on the way out keeps the register count down).
+      for (;;) {
+        if (c1 >= pool_tiles) break;
+        // v is set and read by thread 0 only: left unset elsewhere, it needs
+        // no copy where the branch rejoins (a copy would wait for the atomic,
+        // and with it for every load issued before it).  The claim is an
+        // increment (inc with no wrap bound) rather than an add, which the
+        // compiler would rewrite into a wave-wide add whose result it reads
+        // back at once.
+        int32_t v;
+        if (threadIdx.x == 0) v = claim_next(claim);
+        resolve_pool(c1, bb);
+        load_pool(c1, bb, rb);
+        process_tile(ra);
+        // Two claim slots: a slot is written again only after the barrier
+        // that follows the other slot's write, which every wave reaches after
+        // reading this one.
+        if (threadIdx.x == 0) s_claim[slot] = v;
+        __syncthreads();
+        const int32_t c2 = __builtin_amdgcn_readfirstlane(s_claim[slot]);
+        slot ^= 1;
+        if (c2 >= pool_tiles) {
+          copy_tile(rb, ra);
+          break;
+        }
+        if (threadIdx.x == 0) v = claim_next(claim);
+        resolve_pool(c2, ba);
+        load_pool(c2, ba, ra);
+        process_tile(rb);
+        if (threadIdx.x == 0) s_claim[slot] = v;
+        __syncthreads();
+        c1 = __builtin_amdgcn_readfirstlane(s_claim[slot]);
+        slot ^= 1;
+      }
+      process_tile(ra);
+    }
+    if (bad_blk) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
   }
 
   ODA_PHASE(4);
