@@ -136,13 +136,34 @@ void choose_splits(const oda_dims* d, int32_t batch, Plan* p) {
   }
 }
 
-WsLayout layout(const Plan& p, int32_t batch) {
+// Partial-slot rows (request, query head, split) that a call with any batch
+// up to max_batch uses.  Below 256 / Hkv requests the split counts change with
+// the batch; above it they are constant, so the product grows with the batch.
+int64_t max_partial_rows(const oda_dims* d, const Plan& p0) {
+  int64_t best = 0;
+  auto at = [&](int32_t b) {
+    Plan q = p0;
+    choose_splits(d, b, &q);
+    int32_t ms = q.full_splits;
+    if (q.local_splits > ms) ms = q.local_splits;
+    if (q.sw_splits > ms) ms = q.sw_splits;
+    if ((int64_t)b * ms > best) best = (int64_t)b * ms;
+  };
+  const int32_t lim = p0.max_batch < 256 ? p0.max_batch : 256;
+  for (int32_t b = 1; b <= lim; ++b) at(b);
+  at(p0.max_batch);
+  return best * p0.Hq;
+}
+
+// The workspace layout depends on the dims alone, not on a call's batch: its
+// words are sized for max_batch requests and its partial slots for the
+// largest set any batch up to max_batch uses, so calls with different batches
+// can share one prepared workspace (a slot always lies in the area that was
+// marked empty, never on a counter word of another batch's layout).
+WsLayout layout(const oda_dims* d, const Plan& p) {
   WsLayout w{};
-  const int32_t b = batch > 0 ? batch : 1;
-  int32_t ms = p.full_splits;
-  if (p.local_splits > ms) ms = p.local_splits;
-  if (p.sw_splits > ms) ms = p.sw_splits;
-  w.max_splits = ms;
+  const int32_t b = p.max_batch > 0 ? p.max_batch : 1;
+  const int64_t rows = max_partial_rows(d, p);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.err_off = 0;
   w.count_off = 4;
@@ -153,10 +174,12 @@ WsLayout layout(const Plan& p, int32_t batch) {
   w.claim_off = up(w.ticket_off + sizeof(int32_t) * (size_t)b * p.Hkv);
   // one tail-pool counter per (request, KV head), each on its own 256-byte line
   w.commit_ticket_off = up(w.claim_off + sizeof(int32_t) * oda::kCounterStride * (size_t)b * p.Hkv);
-  w.part_o_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
-  w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)b * p.Hq * ms * p.D);
+  // grid barrier of the one-launch Full section: count, generation, broken flag, a line each
+  w.barrier_off = up(w.commit_ticket_off + sizeof(int32_t) * (size_t)b);
+  w.part_o_off = up(w.barrier_off + 3 * 256);
+  w.part_ml_off = up(w.part_o_off + sizeof(float) * (size_t)rows * p.D);
   const size_t ml_copies = p.D >= 64 ? (size_t)p.D / 64 : 1;  // one (m, l) per merging wave
-  w.total = up(w.part_ml_off + sizeof(float) * 2 * ml_copies * (size_t)b * p.Hq * ms);
+  w.total = up(w.part_ml_off + sizeof(float) * 2 * ml_copies * (size_t)rows);
   return w;
 }
 
@@ -174,7 +197,7 @@ oda_status prepare(const oda_dims* dims, int32_t batch, void* workspace, size_t 
   if (st != ODA_OK) return st;
   if (batch < 0 || batch > c->plan.max_batch) return ODA_ERR_INVALID_ARG;
   choose_splits(dims, batch, &c->plan);
-  c->ws = layout(c->plan, batch);
+  c->ws = layout(dims, c->plan);
   if (need_ws) {
     if (!workspace || ws_bytes < c->ws.total) return ODA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return ODA_ERR_WORKSPACE;
@@ -207,11 +230,10 @@ oda_status hip_status(int rc) { return rc == 0 ? ODA_OK : ODA_ERR_HIP; }
 // Attention pass of one layer.  gate: kGateAll (Local pass of every active
 // request), kGateList (Full pass of the step's compacted list) or kGateBallot
 // (Full pass that compacts score > theta itself).
-oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, int32_t gate,
-                    const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
-                    const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
-                    const float* score, float theta, int32_t* list_out, int32_t* count_out,
-                    oda_stream s) {
+oda::AttnParams make_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, int32_t gate,
+                          const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
+                          const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
+                          const float* score, float theta, int32_t* list_out, int32_t* count_out) {
   const Plan& p = c.plan;
   const bool gated = p.kind[layer] == ODA_LAYER_GATED;
   const bool full = gate != oda::kGateAll;
@@ -271,7 +293,17 @@ oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;
-  return hip_status(oda::launch_attention(p, a, batch, s));
+  return a;
+}
+
+oda_status run_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t batch, int32_t gate,
+                    const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
+                    const int32_t* call_list, const int32_t* call_count, const int32_t* call_len,
+                    const float* score, float theta, int32_t* list_out, int32_t* count_out,
+                    oda_stream s) {
+  const oda::AttnParams a = make_pass(c, kv, layer, batch, gate, q, k_cur, v_cur, out, lse, call_list, call_count,
+                                      call_len, score, theta, list_out, count_out);
+  return hip_status(oda::launch_attention(c.plan, a, batch, s));
 }
 
 oda_status check_head(const oda_recall_head* h) {
@@ -337,12 +369,34 @@ oda_status run_step(const Ctx& c, const oda_kv* kv, int32_t batch, const void* q
                             stream);
   if (rc) return ODA_ERR_HIP;
   // 4) Full recomputation of every layer for the fired requests, dispatched
-  //    longest first.
-  for (int32_t l = 0; l < p.L; ++l) {
-    st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
-                  at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
-                  order, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
-    if (st != ODA_OK) return st;
+  //    longest first.  When every layer is gated and a layer's workgroups fit
+  //    the chip at once, the whole section is one launch: nothing runs when
+  //    nothing fired, and otherwise the layers follow each other inside it.
+  const oda::AttnParams a0 = make_pass(c, kv, 0, batch, oda::kGateList, qf, k_new, v_new, out, lse, order, count,
+                                       lens, nullptr, 0.f, nullptr, nullptr);
+  const int64_t groups = (int64_t)a0.splits * p.Hkv * batch;
+  const int cus = oda::compute_units();
+  if (p.Ls == 0 && cus > 0 && groups <= cus && groups <= kComputeUnits) {
+    oda::RegionParams r{};
+    r.layers = p.L;
+    r.groups = (uint32_t)groups;
+    r.cache_layer_bytes = kv->num_blocks * p.Hkv * p.block_size * (int64_t)p.D * p.esize;
+    r.q_layer_bytes = q_layer;
+    r.kv_layer_bytes = kv_layer;
+    r.o_layer = o_layer;
+    r.l_layer = l_layer;
+    r.bar_count = reinterpret_cast<uint32_t*>(c.base + c.ws.barrier_off);
+    r.bar_gen = reinterpret_cast<uint32_t*>(c.base + c.ws.barrier_off + 256);
+    r.bar_broken = reinterpret_cast<uint32_t*>(c.base + c.ws.barrier_off + 512);
+    r.err = c.err;
+    if (oda::launch_full_section(p, a0, r, batch, stream)) return ODA_ERR_HIP;
+  } else {
+    for (int32_t l = 0; l < p.L; ++l) {
+      st = run_pass(c, kv, l, batch, oda::kGateList, at(qf, l * q_layer), at(k_new, l * kv_layer),
+                    at(v_new, l * kv_layer), out + l * o_layer, lse ? lse + l * l_layer : nullptr,
+                    order, count, lens, nullptr, 0.f, nullptr, nullptr, stream);
+      if (st != ODA_OK) return st;
+    }
   }
   // 5) Fused commit of position t for all layers.
   return hip_status(oda::launch_commit(p, *kv, batch, k_new, v_new,

@@ -39,9 +39,8 @@ struct Plan {
 
 // Workspace carve-up for `batch` requests.
 struct WsLayout {
-  size_t err_off, count_off, list_off, order_off, len_off, ticket_off, claim_off, commit_ticket_off, part_o_off, part_ml_off,
-      total;
-  int32_t max_splits;
+  size_t err_off, count_off, list_off, order_off, len_off, ticket_off, claim_off, commit_ticket_off, barrier_off,
+      part_o_off, part_ml_off, total;
 };
 
 // Which rows a pass scans and how they map to positions.
@@ -102,8 +101,28 @@ struct AttnParams {
   float v_scale;              // applied to the merged output
 };
 
+// The Full section of a step in one launch: layer l of `layers` (all gated)
+// reads the cache, queries, current token and outputs at l strides from
+// those of layer 0 in AttnParams; the layers are separated by a barrier of
+// the whole grid.
+struct RegionParams {
+  int32_t layers;
+  uint32_t groups;             // workgroups of the launch
+  int64_t cache_layer_bytes;   // paged cache, K and V alike
+  int64_t q_layer_bytes;
+  int64_t kv_layer_bytes;      // the current token's K / V
+  int64_t o_layer, l_layer;    // floats
+  uint32_t* bar_count;         // workspace words, each on its own 256-byte line,
+  uint32_t* bar_gen;           // zero (count, broken) when the launch starts
+  uint32_t* bar_broken;
+  uint32_t* err;
+};
+
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
+int launch_full_section(const Plan& p, const AttnParams& a, const RegionParams& r, int32_t batch, oda_stream s);
+// Compute units of the current device (0 if the runtime cannot tell).
+int compute_units();
 // call_list (ascending; needed when disp_list is given) and call_count are the
 // compacted decisions; disp_list / disp_len (nullable) the fired requests and
 // their committed lengths in the Full passes' dispatch order (longest first).

@@ -618,13 +618,17 @@ __device__ __forceinline__ bool merge_output(const AttnParams& P, int32_t b, int
       __builtin_amdgcn_s_sleep(1);
     }
     {
-      // The round's slots are read: this wave leaves what it read empty for the
-      // next launch (plain 16-byte stores; the launch boundary publishes them):
-      // its 64 elements of each of the n rows of o, and its copy of (m, l).
-      float4* ro = reinterpret_cast<float4*>(P.part_o + ((head0 + h) * P.splits + base) * D) + half * (kWave / 4);
-      const float4 e4 = make_float4(empty, empty, empty, empty);
-      for (int32_t i = lane; i < n * (kWave / 4); i += kWave) ro[(i / (kWave / 4)) * (D / 4) + i % (kWave / 4)] = e4;
-      if (lane < n) *reinterpret_cast<float2*>(ml + 2 * kCopies * (base + lane)) = make_float2(empty, empty);
+      // The round's slots are read: this wave leaves what it read empty for
+      // the next pass, its 64 elements of each of the n rows of o and its copy
+      // of (m, l).  Device-scope stores, like the partials themselves: no
+      // dirty line of them stays in this XCD's L2, where a later write-back
+      // could land on a partial stored after them.
+      float* ro = P.part_o + ((head0 + h) * P.splits + base) * D + half * kWave;
+      for (int32_t i = 0; i < n; ++i) publish(ro + (int64_t)i * D + lane, empty);
+      if (lane < n) {
+        publish(ml + 2 * kCopies * (base + lane), empty);
+        publish(ml + 2 * kCopies * (base + lane) + 1, empty);
+      }
     }
     const float m_new = fmaxf(M, wave_max(mi));
     const float keep = M == -INFINITY ? 0.f : fast_exp2(M - m_new);
@@ -668,7 +672,7 @@ __device__ __forceinline__ bool merge_and_write(const AttnParams& P, int32_t b, 
 // passes).  Without it, a ring pass that loops over many tiles keeps its loads
 // in flight across the joins.
 template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
-__global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
+__device__ __forceinline__ void attention_pass(const AttnParams& P) {
   using Gm = Geo<DT, D, SRC, G>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
@@ -1483,6 +1487,84 @@ __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) 
   }
 }
 
+template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
+__global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
+  attention_pass<DT, D, G, SRC, BALLOT, SKIP>(P);
+}
+
+// ----------------------------------------------------------------------------
+// the Full section of a decode step in one launch
+
+// Every workgroup of the launch waits here until all have arrived (the launch
+// must fit the chip at once; the host checks).  Thread 0 reads the generation
+// before arriving, so the last arrival's bump cannot be missed; the last
+// arrival clears the count before the bump, so the next barrier starts from
+// zero.  A wait that exceeds the spin limit marks the launch broken
+// (ODA_DEVERR_MERGE_WAIT) and every workgroup leaves.
+constexpr int32_t kBarrierSpinLimit = 1 << 20;
+__device__ __forceinline__ bool grid_barrier(const RegionParams& R) {
+  // Every wave's device-scope stores of the layer (partials, the empty marks
+  // of its merge, counter resets) have completed before the arrival.  The
+  // only data another workgroup reads after the barrier is read with
+  // device-scope loads, so no cache-wide fence is needed (one per wave and
+  // layer costs tens of microseconds).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ int32_t s_ok;
+  if (threadIdx.x == 0) {
+    const uint32_t gen = __hip_atomic_load(R.bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t arrived = __hip_atomic_fetch_add(R.bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t ok = 1;
+    if (arrived + 1 == R.groups) {
+      __hip_atomic_store(R.bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clear lands before the release of the others
+      __hip_atomic_fetch_add(R.bar_gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      for (int32_t spin = 0;; ++spin) {
+        // relaxed polls (an acquire load would invalidate the L2 on every poll)
+        if (__hip_atomic_load(R.bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen) break;
+        if (__hip_atomic_load(R.bar_broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          ok = 0;
+          break;
+        }
+        if (spin == kBarrierSpinLimit) {
+          __hip_atomic_store(R.bar_broken, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          atomicOr(R.err, (uint32_t)ODA_DEVERR_MERGE_WAIT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// The Full pass of every layer of a step (all layers gated, one round of
+// workgroups): when the gate fired no request the whole grid leaves at once,
+// in place of one empty launch per layer; otherwise the layers run in order,
+// each after the previous one's merge, as separate launches would run them.
+// P describes layer 0; layer l's cache, queries, current token and outputs
+// sit l strides further.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kGroupThreads) void full_section_kernel(AttnParams P, RegionParams R) {
+  if (*P.call_count <= 0) return;
+  for (int32_t l = 0; l < R.layers; ++l) {
+    AttnParams Pl = P;
+    Pl.k_base = static_cast<const char*>(P.k_base) + l * R.cache_layer_bytes;
+    Pl.v_base = static_cast<const char*>(P.v_base) + l * R.cache_layer_bytes;
+    Pl.q = static_cast<const char*>(P.q) + l * R.q_layer_bytes;
+    Pl.k_cur = static_cast<const char*>(P.k_cur) + l * R.kv_layer_bytes;
+    Pl.v_cur = static_cast<const char*>(P.v_cur) + l * R.kv_layer_bytes;
+    Pl.out = P.out + l * R.o_layer;
+    Pl.lse = P.lse != nullptr ? P.lse + l * R.l_layer : nullptr;
+    attention_pass<DT, D, G, kSrcPaged, false, true>(Pl);
+    if (l + 1 < R.layers && !grid_barrier(R)) return;
+  }
+}
+
 // ----------------------------------------------------------------------------
 // gate: compaction of the fired requests + accounting
 
@@ -1927,6 +2009,13 @@ int launch_attention_t(const AttnParams& a, int32_t batch, oda_stream s) {
   return (int)hipGetLastError();
 }
 
+template <int DT, int D, int G>
+int launch_full_section_t(const AttnParams& a, const RegionParams& r, int32_t batch, oda_stream s) {
+  dim3 grid(a.splits, a.Hkv, batch);
+  hipLaunchKernelGGL((full_section_kernel<DT, D, G>), grid, dim3(kGroupThreads), 0, s, a, r);
+  return (int)hipGetLastError();
+}
+
 // Groups of 8 are built for bf16 and FP8 (both products on MFMA) and for f32
 // with d = 64, whose row fits one 16-byte chunk per lane of a 16-lane row with
 // eight heads' accumulators (the host reports f32 with d = 128 unsupported).
@@ -1976,6 +2065,47 @@ int tile_rows_g(int32_t dtype, int32_t head_dim, int32_t group) {
 int tile_rows_for(int32_t dtype, int32_t head_dim, int32_t source, int32_t group) {
   return source == kSrcRing ? tile_rows_g<kSrcRing>(dtype, head_dim, group)
                             : tile_rows_g<kSrcPaged>(dtype, head_dim, group);
+}
+
+template <int DT, int D>
+int launch_full_section_d(const Plan& p, const AttnParams& a, const RegionParams& r, int32_t batch, oda_stream s) {
+  switch (p.G) {
+    case 1: return launch_full_section_t<DT, D, 1>(a, r, batch, s);
+    case 2: return launch_full_section_t<DT, D, 2>(a, r, batch, s);
+    case 4: return launch_full_section_t<DT, D, 4>(a, r, batch, s);
+    case 8:
+      if constexpr (kGroup8Built<DT, D>) return launch_full_section_t<DT, D, 8>(a, r, batch, s);
+      return (int)hipErrorInvalidValue;
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_full_section(const Plan& p, const AttnParams& a, const RegionParams& r, int32_t batch, oda_stream s) {
+  if (batch <= 0) return 0;
+  if (p.dtype == ODA_BF16) {
+    if (p.D == 128) return launch_full_section_d<ODA_BF16, 128>(p, a, r, batch, s);
+    return launch_full_section_d<ODA_BF16, 64>(p, a, r, batch, s);
+  }
+  if (p.dtype == ODA_FP8_E4M3) {
+    if (p.D == 128) return launch_full_section_d<ODA_FP8_E4M3, 128>(p, a, r, batch, s);
+    return launch_full_section_d<ODA_FP8_E4M3, 64>(p, a, r, batch, s);
+  }
+  if (p.D == 128) return launch_full_section_d<ODA_F32, 128>(p, a, r, batch, s);
+  return launch_full_section_d<ODA_F32, 64>(p, a, r, batch, s);
+}
+
+int compute_units() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s) {

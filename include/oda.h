@@ -137,13 +137,17 @@ typedef struct {
   int64_t num_blocks;          /* physical blocks per layer in k_cache / v_cache         */
 } oda_kv;
 
-/* Host.  Bytes of workspace any call below needs for `batch` requests (the
- * first 256 bytes hold the device error word).  0 on invalid dims. */
+/* Host.  Bytes of workspace the calls below need (the first 256 bytes hold
+ * the device error word).  The layout depends on the dims alone: it is sized
+ * for any batch up to dims->max_batch, so calls with different batches can
+ * share one prepared workspace.  `batch` is only validated.  0 on invalid
+ * dims or batch. */
 size_t oda_workspace_size(const oda_dims* dims, int32_t batch);
 
 /* Prepares the workspace (small kernels; call once after allocating it): zeroes
- * the error word, the ticket words and the tail-tile counters, and marks every
- * split-partial slot empty.  Between launches the tickets and counters read
+ * the error word, the ticket words, the tail-tile counters and the barrier
+ * words of the one-launch Full section, and marks every split-partial slot
+ * empty.  Between launches the tickets and counters read
  * zero and the slots read empty: each launch's merging workgroup finds the
  * other splits' partials by a ticket (any launch size) or by re-reading slots
  * until none is empty (launches whose workgroups are all resident at once),
@@ -223,7 +227,11 @@ oda_status oda_gate(const oda_dims* dims, const oda_kv* kv, int32_t batch,
  * cross-layer KV commit; learnaivisually explainer, runtime paragraph: the
  * recalled step still pays the Local attempt): the Local pass of every layer,
  * the gate (with accounting), the Full pass of every layer for the fired
- * requests, then the fused commit.  q_local / q_full
+ * requests, then the fused commit.  When every layer is gated and a layer's
+ * Full pass fits the chip in one round of workgroups, the Full passes of all
+ * layers are one launch: it ends at once when no request fired, and otherwise
+ * runs the layers in order, each after the previous layer's merge (a barrier
+ * of the whole grid); otherwise each layer has its own launch.  q_local / q_full
  * [L][batch][Hq][d] (q_full NULL: reuse q_local), k_new / v_new
  * [L][batch][Hkv][d], out [L][batch][Hq][d] (the accepted result), lse
  * [L][batch][Hq] (nullable).  Capture it once into a HIP graph and replay it
