@@ -859,21 +859,56 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
   // -1 marks a row outside the pass (or a block id the table gets wrong).
   struct BlockIds {
     int32_t blk[NP];
+    bool ok[NP];  // the row is in the pass (blk was read for it)
   };
+  // Paged passes read every lane's table entry and K/V rows unconditionally:
+  // a row outside the pass reads position 1's entry and the current token's
+  // row, and is masked when the tile is reduced.  Loads on conditional paths
+  // make the compiler wait for every outstanding load before the next one, so
+  // with them a wave keeps one tile in flight instead of two.
+  uint32_t bad_blk = 0;
   auto resolve_blocks = [&](int32_t tile, BlockIds& B) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       B.blk[i] = -1;
+      B.ok[i] = false;
       if constexpr (SRC == kSrcPaged) {
         const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP + rrow;
-        if (tile < n_tiles && row < row_end && row < n_rows) {
-          const int32_t p = interval_position(iv, row);
-          B.blk[i] = btab[(p - 1) >> P.block_shift];
-        }
+        const bool in = tile < n_tiles && row < row_end && row < n_rows;
+        const int32_t p = interval_position(iv, in ? row : 0);
+        B.blk[i] = btab[(p - 1) >> P.block_shift];
+        B.ok[i] = in;
       }
     }
   };
   auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R) {
+    if constexpr (SRC == kSrcPaged) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int32_t pass0 = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP;
+        const int32_t row = pass0 + rrow;
+        R.row[i] = row;
+        R.live[i] = !SKIP || pass0 < row_end;
+        const int32_t blk = B.blk[i];
+        const bool blk_ok = blk >= 0 && (int64_t)blk < P.num_blocks;
+        bad_blk |= B.ok[i] && !blk_ok;
+        const bool from_cache = B.ok[i] && blk_ok;
+        R.valid[i] = from_cache || (row == n_rows && row < row_end);
+        const int32_t r0 = interval_position(iv, from_cache ? row : 0) - 1;
+        const char* kb = from_cache ? kbase : static_cast<const char*>(P.k_cur);
+        const char* vb = from_cache ? vbase : static_cast<const char*>(P.v_cur);
+        const int64_t off =
+            from_cache ? ((((int64_t)g * P.num_blocks + blk) << P.block_shift) + (r0 & bmask)) * D * ES : cur_off;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          // non-temporal where a load instruction covers whole 128-byte lines
+          constexpr bool kStream = LPR * 16 >= 128;
+          R.k[i][j] = kv_load<kStream>(kb + off + (j * LPR + sub) * 16);
+          R.v[i][j] = kv_load<kStream>(vb + off + (j * LPR + sub) * 16);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP + rrow;
@@ -896,28 +931,15 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
         kb = static_cast<const char*>(P.k_cur);
         vb = static_cast<const char*>(P.v_cur);
         off = cur_off;
-      } else if constexpr (SRC == kSrcRing) {
-        off = ring_head_off + (int64_t)row * D * ES;
       } else {
-        if (ok) {
-          const int32_t r0 = interval_position(iv, row) - 1;
-          const int32_t blk = B.blk[i];
-          if (blk < 0 || (int64_t)blk >= P.num_blocks) {
-            atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
-            ok = false;
-          } else {
-            off = ((((int64_t)g * P.num_blocks + blk) << P.block_shift) + (r0 & bmask)) * D * ES;
-          }
-        }
+        off = ring_head_off + (int64_t)row * D * ES;
       }
       R.valid[i] = ok;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         if (ok) {
-          // non-temporal where a load instruction covers whole 128-byte lines
-          constexpr bool kStream = SRC == kSrcRing || LPR * 16 >= 128;
-          R.k[i][j] = kv_load<kStream>(kb + off + (j * LPR + sub) * 16);
-          R.v[i][j] = kv_load<kStream>(vb + off + (j * LPR + sub) * 16);
+          R.k[i][j] = kv_load<true>(kb + off + (j * LPR + sub) * 16);
+          R.v[i][j] = kv_load<true>(vb + off + (j * LPR + sub) * 16);
         } else {
           R.k[i][j] = make_uint4(0, 0, 0, 0);
           R.v[i][j] = make_uint4(0, 0, 0, 0);
@@ -1163,7 +1185,10 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
   BlockIds ba, bb;
   if (spec_hit) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) ba.blk[i] = spec_blk[i];
+    for (int i = 0; i < NP; ++i) {  // the first tile lies inside the split and before the current token
+      ba.blk[i] = spec_blk[i];
+      ba.ok[i] = true;
+    }
   } else {
     resolve_blocks(0, ba);
   }
@@ -1219,7 +1244,6 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
       if (threadIdx.x == 0) s_claim[0] = first;
       __syncthreads();
     }
-    uint32_t bad_blk = 0;
     auto resolve_pool = [&](int32_t c, BlockIds& B) {
       const int32_t r0 = n_static + c * TILE;
 #pragma unroll
@@ -1303,8 +1327,9 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
       }
       process_tile(ra);
     }
-    if (bad_blk) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
   }
+  if constexpr (SRC == kSrcPaged)
+    if (bad_blk) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
 
   ODA_PHASE(4);
   constexpr int FOLD_ROWS = kWavesPerGroup;  // rows of the LDS fold: one per wave
