@@ -285,8 +285,8 @@ oda::AttnParams make_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t
   // workgroup waits for the others): one per compute unit at most.  Such a
   // launch also balances its tail through the pool of tail tiles; larger ones
   // already balance through the dispatch of later workgroups.  FP8 passes keep
-  // static splits: with the pool they measured 2-5% slower at 128K (groups of
-  // 2, 4 and 8).
+  // static splits: with the pool they measured no faster at 128K (groups of 2,
+  // 4 and 8).
   const bool one_round = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits;
   a.merge_mode = one_round && !c.ticket_only ? oda::kMergePoll : oda::kMergeTicket;
   a.claims = one_round && p.dtype != ODA_FP8_E4M3 ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
