@@ -284,12 +284,13 @@ oda::AttnParams make_pass(const Ctx& c, const oda_kv* kv, int32_t layer, int32_t
   // Polling needs every workgroup of the launch resident at once (the merging
   // workgroup waits for the others): one per compute unit at most.  Such a
   // launch also balances its tail through the pool of tail tiles; larger ones
-  // already balance through the dispatch of later workgroups.  FP8 passes keep
-  // static splits: with the pool they measured no faster at 128K (groups of 2,
-  // 4 and 8).
+  // already balance through the dispatch of later workgroups.  FP8 passes of
+  // GQA groups of 4 and 8 (MFMA) keep static splits: with the pool they measured
+  // about 1 us slower per launch at 128K, where it saves 1 us at group 2.
   const bool one_round = (int64_t)a.splits * p.Hkv * batch <= kComputeUnits;
   a.merge_mode = one_round && !c.ticket_only ? oda::kMergePoll : oda::kMergeTicket;
-  a.claims = one_round && p.dtype != ODA_FP8_E4M3 ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
+  const bool pool = one_round && !(p.dtype == ODA_FP8_E4M3 && p.G >= 4);
+  a.claims = pool ? reinterpret_cast<int32_t*>(c.base + c.ws.claim_off) : nullptr;
   a.err = c.err;
   a.scale_log2 = p.scale_log2;
   a.v_scale = p.v_scale;

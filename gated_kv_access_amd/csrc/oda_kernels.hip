@@ -867,13 +867,13 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
   // make the compiler wait for every outstanding load before the next one, so
   // with them a wave keeps one tile in flight instead of two.
   uint32_t bad_blk = 0;
-  auto resolve_blocks = [&](int32_t tile, BlockIds& B) {
+  auto resolve_blocks = [&](int32_t tile, BlockIds& B, int32_t slot) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       B.blk[i] = -1;
       B.ok[i] = false;
       if constexpr (SRC == kSrcPaged) {
-        const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP + rrow;
+        const int32_t row = row_begin + tile * TILE + (i * kWavesPerGroup + slot) * RPP + rrow;
         const bool in = tile < n_tiles && row < row_end && row < n_rows;
         const int32_t p = interval_position(iv, in ? row : 0);
         B.blk[i] = btab[(p - 1) >> P.block_shift];
@@ -881,11 +881,11 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
       }
     }
   };
-  auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R) {
+  auto load_tile = [&](int32_t tile, const BlockIds& B, TileRegs& R, int32_t slot) {
     if constexpr (SRC == kSrcPaged) {
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int32_t pass0 = row_begin + tile * TILE + (i * kWavesPerGroup + wave) * RPP;
+        const int32_t pass0 = row_begin + tile * TILE + (i * kWavesPerGroup + slot) * RPP;
         const int32_t row = pass0 + rrow;
         R.row[i] = row;
         R.live[i] = !SKIP || pass0 < row_end;
@@ -1190,10 +1190,61 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
       ba.ok[i] = true;
     }
   } else {
-    resolve_blocks(0, ba);
+    resolve_blocks(0, ba, wave);
   }
-  resolve_blocks(1, bb);
-  load_tile(0, ba, ra);
+  if constexpr (SRC == kSrcPaged) {
+    // The static share in wave units: unit u is slot u mod 8 of tile u / 8
+    // (the rows a wave covers in one tile).  Each wave starts with its own slot
+    // of the first two tiles and then takes the next unit from a workgroup
+    // counter in LDS, so a wave whose loads return late takes fewer units and
+    // the waves of a workgroup finish closer together (at 128K, FP8: the last
+    // wave of a workgroup about 3 us after the first instead of 5; the Full
+    // launch 1 us shorter).  An LDS atomic does not wait on the wave's global
+    // loads.  Units are claimed two ahead of their loads
+    // and their block ids looked up one half-iteration ahead, as in the tile
+    // loop; the loads stay unconditional.
+    __shared__ int32_t s_unit;
+    if (threadIdx.x == 0) s_unit = 2 * kWavesPerGroup;
+    __syncthreads();
+    const int32_t n_units = n_tiles * kWavesPerGroup;
+    auto claim_unit = [&]() {
+      int32_t v = 0;
+      if (lane == 0) v = atomicAdd(&s_unit, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    auto resolve_unit = [&](int32_t u, BlockIds& B) {
+      resolve_blocks(u / kWavesPerGroup, B, u % kWavesPerGroup);
+    };
+    auto load_unit = [&](int32_t u, const BlockIds& B, TileRegs& R) {
+      load_tile(u / kWavesPerGroup, B, R, u % kWavesPerGroup);
+    };
+    int32_t ub = kWavesPerGroup + wave;
+    resolve_unit(ub, bb);
+    load_tile(0, ba, ra, wave);
+    int32_t uc = claim_unit();
+    if (wave < n_units) {
+      // ra holds a loaded unit, bb the block ids of unit ub, uc is claimed.
+      for (;;) {
+        if (ub >= n_units) break;
+        resolve_unit(uc, ba);
+        load_unit(ub, bb, rb);
+        process_tile(ra);
+        const int32_t ud = claim_unit();
+        if (uc >= n_units) {
+          copy_tile(rb, ra);
+          break;
+        }
+        resolve_unit(ud, bb);
+        load_unit(uc, ba, ra);
+        process_tile(rb);
+        ub = ud;
+        uc = claim_unit();
+      }
+      process_tile(ra);
+    }
+  } else {
+  resolve_blocks(1, bb, wave);
+  load_tile(0, ba, ra, wave);
   if constexpr (SRC == kSrcRing) {
     if (P.gate_mode == kGateAll) committed = P.seq_len[b];
     if (committed < 0) return;
@@ -1203,13 +1254,14 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
   }
   for (int32_t tile = 0; tile < n_tiles; tile += 2) {
     const bool has_b = tile + 1 < n_tiles;
-    resolve_blocks(tile + 2, ba);
-    if (has_b) load_tile(tile + 1, bb, rb);
+    resolve_blocks(tile + 2, ba, wave);
+    if (has_b) load_tile(tile + 1, bb, rb, wave);
     process_tile(ra);
     if (tile == 0) ODA_PHASE(2);
-    resolve_blocks(tile + 3, bb);
-    if (tile + 2 < n_tiles) load_tile(tile + 2, ba, ra);
+    resolve_blocks(tile + 3, bb, wave);
+    if (tile + 2 < n_tiles) load_tile(tile + 2, ba, ra, wave);
     if (has_b) process_tile(rb);
+  }
   }
   ODA_PHASE(3);
   if (n_static < n_all) {
