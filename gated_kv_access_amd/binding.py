@@ -29,7 +29,7 @@ EXPORTS = ("oda_workspace_size", "oda_workspace_init", "oda_prefill_kv", "oda_ri
            "oda_step_static",
            "oda_access_set", "oda_stage_step", "oda_advance_counter", "oda_host_kv_pointer",
            "oda_recall_workspace_size", "oda_recall_workspace_init", "oda_recall_scores", "oda_step_recall",
-           "oda_status_string")
+           "oda_test_merge_wait", "oda_status_string")
 
 
 class OdaError(RuntimeError):
@@ -105,6 +105,7 @@ def load(path: str = LIB_PATH):
         "oda_recall_scores": (I32, [ctypes.POINTER(OdaRecallHead), I32, P, P, P, SZ, P]),
         "oda_step_recall": (I32, [D, K, I32, P, P, P, P, ctypes.POINTER(OdaRecallHead), P, P, F, P, P, P, P,
                                   P, P, P, SZ, P, SZ, P]),
+        "oda_test_merge_wait": (I32, [D, K, I32, I32, P, P, P, P, P, I32, I32, P, SZ, P]),
         "oda_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sig.items():
@@ -172,6 +173,13 @@ def decode_local(dims, kv, layer, batch, q, k_cur, v_cur, out, lse, ws, stream=N
     _check("oda_decode_local", load().oda_decode_local(
         ctypes.byref(dims), ctypes.byref(kv), layer, batch, _p(q), _p(k_cur), _p(v_cur), _p(out),
         _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def test_merge_wait(dims, kv, layer, batch, q, k_cur, v_cur, out, lse, withheld_split, spin_limit, ws,
+                    stream=None) -> None:
+    _check("oda_test_merge_wait", load().oda_test_merge_wait(
+        ctypes.byref(dims), ctypes.byref(kv), layer, batch, _p(q), _p(k_cur), _p(v_cur), _p(out), _p(lse),
+        int(withheld_split), int(spin_limit), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def decode_full_gated(dims, kv, layer, batch, q, k_cur, v_cur, recall_score, theta, out, lse,

@@ -472,6 +472,25 @@ oda_status oda_decode_local(const oda_dims* dims, const oda_kv* kv, int32_t laye
                   nullptr, 0.f, nullptr, nullptr, stream);
 }
 
+oda_status oda_test_merge_wait(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
+                               const void* q, const void* k_cur, const void* v_cur, float* out, float* lse,
+                               int32_t withheld_split, int32_t spin_limit, void* workspace,
+                               size_t workspace_bytes, oda_stream stream) {
+  Ctx c;
+  oda_status st = prepare(dims, batch, workspace, workspace_bytes, &c);
+  if (st != ODA_OK) return st;
+  if (layer < 0 || layer >= c.plan.L || !q || !k_cur || !v_cur || !out) return ODA_ERR_INVALID_ARG;
+  if (!aligned16(q) || spin_limit < 0 || withheld_split < 0) return ODA_ERR_INVALID_ARG;
+  st = check_kv(c.plan, kv, false, true);
+  if (st != ODA_OK) return st;
+  if (batch == 0) return ODA_OK;
+  const oda::AttnParams a = make_pass(c, kv, layer, batch, oda::kGateAll, q, k_cur, v_cur, out, lse, nullptr,
+                                      nullptr, nullptr, nullptr, 0.f, nullptr, nullptr);
+  if (a.merge_mode != oda::kMergePoll || withheld_split + 1 >= a.splits) return ODA_ERR_UNSUPPORTED;
+  if (c.plan.dtype != ODA_BF16 || c.plan.G > 2) return ODA_ERR_UNSUPPORTED;
+  return hip_status(oda::launch_attention_merge_wait(c.plan, a, batch, withheld_split, spin_limit, stream));
+}
+
 oda_status oda_decode_full_gated(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
                                  const void* q, const void* k_cur, const void* v_cur,
                                  const float* recall_score, float theta, float* out, float* lse,

@@ -66,6 +66,10 @@ enum MergeMode : int32_t {
                      // resident at once)
 };
 
+// Re-reads of the partial slots the merging workgroup of a polling pass makes
+// (about a second) before it gives up.
+constexpr int32_t kMergeSpinLimit = 1 << 20;
+
 // One attention pass of one layer: split-K partials, then one workgroup of
 // each (request, KV head) merges them.
 struct AttnParams {
@@ -120,6 +124,11 @@ struct RegionParams {
 
 // Launchers (oda_kernels.hip).  Each returns hipGetLastError() as an int.
 int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stream s);
+// A ring pass (bf16, GQA groups 1 and 2) whose split `withheld` stores no
+// partial and whose merging workgroups give up after `spin_limit` re-reads:
+// the test of the merge's failure path.  Other shapes: hipErrorInvalidValue.
+int launch_attention_merge_wait(const Plan& p, const AttnParams& a, int32_t batch, int32_t withheld,
+                                int32_t spin_limit, oda_stream s);
 int launch_full_section(const Plan& p, const AttnParams& a, const RegionParams& r, int32_t batch, oda_stream s);
 // Compute units of the current device (0 if the runtime cannot tell).
 int compute_units();

@@ -468,7 +468,9 @@ __device__ __forceinline__ int32_t interval_position(const Intervals& iv, int32_
 constexpr int32_t kSplitRowUnit = 16;
 // Tail-pool tiles per split (paged passes over long ranges).  At 128K, bf16
 // group 2: the pool saves 2.6 us per Full launch over static splits alone,
-// and pools of 6, 10 and 16 tiles per split measured no faster than 3.
+// and pools of 6, 10 and 16 tiles per split measured no faster than 3.  (At
+// 16K, where a split has 4 tiles, a pool of one tile per split made the
+// launch 1.5 us slower: a pool tile costs a claim and a full round trip.)
 constexpr int32_t kPoolTilesPerSplit = 3;
 // The pool's block ids are staged in LDS when the pool starts; the pool is
 // sized so that they fit.
@@ -559,7 +561,6 @@ __device__ __forceinline__ void write_call_list(const AttnParams& P) {
 // launch whose workgroups are all resident at once therefore needs no flag or
 // counter: it reads the slots and reads again those still empty.
 constexpr uint32_t kPartialEmpty = 0x7FA5A5A5u;
-constexpr int32_t kMergeSpinLimit = 1 << 20;  // about a second of re-reads
 __device__ __forceinline__ bool slot_empty(float x) { return __float_as_uint(x) == kPartialEmpty; }
 
 constexpr int kMergeBatch = 32;  // partials loaded per round by one output thread
@@ -577,7 +578,7 @@ constexpr int kMergeBatch = 32;  // partials loaded per round by one output thre
 // No LDS writes, no barrier.
 template <int DT, int D, int G>
 __device__ __forceinline__ bool merge_output(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
-                             const float* own_o, const float* own_ml, int tid) {
+                             const float* own_o, const float* own_ml, int tid, int32_t spin_limit) {
   const int lane = tid & (kWave - 1);
   const int h = tid / D, e = tid % D;
   const int64_t head0 = (int64_t)b * P.Hq + (int64_t)g * G;
@@ -611,7 +612,7 @@ __device__ __forceinline__ bool merge_output(const AttnParams& P, int32_t b, int
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) missing = missing || slot_empty(x[i]);
       if (!__any(missing)) break;
-      if (spin == kMergeSpinLimit) {
+      if (spin == spin_limit) {
         if (lane == 0) atomicOr(P.err, (uint32_t)ODA_DEVERR_MERGE_WAIT);
         return false;
       }
@@ -657,10 +658,10 @@ __device__ __forceinline__ bool merge_output(const AttnParams& P, int32_t b, int
 
 template <int DT, int D, int G>
 __device__ __forceinline__ bool merge_and_write(const AttnParams& P, int32_t b, int32_t g, int32_t n_mem, bool poll,
-                                const float* own_o, const float* own_ml) {
+                                const float* own_o, const float* own_ml, int32_t spin_limit = kMergeSpinLimit) {
   static_assert(D % kWave == 0, "one head per wave");
   for (int tid = threadIdx.x; tid < G * D; tid += kGroupThreads)
-    if (!merge_output<DT, D, G>(P, b, g, n_mem, poll, own_o, own_ml, tid)) return false;
+    if (!merge_output<DT, D, G>(P, b, g, n_mem, poll, own_o, own_ml, tid, spin_limit)) return false;
   return true;
 }
 
@@ -671,8 +672,12 @@ __device__ __forceinline__ bool merge_and_write(const AttnParams& P, int32_t b, 
 // (the host asks for it when the splits are shorter than a tile, and for paged
 // passes).  Without it, a ring pass that loops over many tiles keeps its loads
 // in flight across the joins.
-template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
-__device__ __forceinline__ void attention_pass(const AttnParams& P) {
+// WITHHOLD (the test of the merge's failure path only): split `withheld`
+// stores no partial and the merging workgroup gives up after `spin_limit`
+// re-reads of the partial slots.
+template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP, bool WITHHOLD = false>
+__device__ __forceinline__ void attention_pass(const AttnParams& P, int32_t withheld = -1,
+                                               int32_t spin_limit = kMergeSpinLimit) {
   using Gm = Geo<DT, D, SRC, G>;
   constexpr int LPR = Gm::LPR, RPP = Gm::RPP, EPV = Gm::EPV, EPL = Gm::EPL, NP = Gm::NP;
   constexpr int NV = Gm::NV, QV = Gm::QV, QPV = Gm::QPV;
@@ -1384,6 +1389,9 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
     if (bad_blk) atomicOr(P.err, (uint32_t)ODA_DEVERR_BLOCK_ID);
 
   ODA_PHASE(4);
+  if constexpr (WITHHOLD) {  // leaves without storing: the merging workgroup waits in vain
+    if (split == withheld && !(P.merge_mode == kMergePoll && split + 1 == used)) return;
+  }
   constexpr int FOLD_ROWS = kWavesPerGroup;  // rows of the LDS fold: one per wave
   __shared__ float s_wmax[kWavesPerGroup][G];
   constexpr int RS = G * D + 4;  // LDS row stride (words)
@@ -1536,7 +1544,7 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
     }
     __syncthreads();
     ODA_PHASE(6);
-    merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0]);
+    merge_and_write<DT, D, G>(P, b, g, used - 1, true, s_own_o, &s_own_ml[0][0], spin_limit);
     ODA_PHASE_STORED(7);
     // every split has published, so none claims pool tiles any more
     if (threadIdx.x == 0 && n_static < n_all)
@@ -1567,6 +1575,12 @@ __device__ __forceinline__ void attention_pass(const AttnParams& P) {
 template <int DT, int D, int G, int SRC, bool BALLOT, bool SKIP>
 __global__ __launch_bounds__(kGroupThreads) void attention_kernel(AttnParams P) {
   attention_pass<DT, D, G, SRC, BALLOT, SKIP>(P);
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kGroupThreads) void merge_wait_test_kernel(AttnParams P, int32_t withheld,
+                                                                        int32_t spin_limit) {
+  attention_pass<DT, D, G, kSrcRing, false, true, true>(P, withheld, spin_limit);
 }
 
 // ----------------------------------------------------------------------------
@@ -2197,6 +2211,22 @@ int launch_attention(const Plan& p, const AttnParams& a, int32_t batch, oda_stre
   }
   if (p.D == 128) return launch_attention_d<ODA_F32, 128>(p, a, batch, s);
   return launch_attention_d<ODA_F32, 64>(p, a, batch, s);
+}
+
+int launch_attention_merge_wait(const Plan& p, const AttnParams& a, int32_t batch, int32_t withheld,
+                                int32_t spin_limit, oda_stream s) {
+  if (batch <= 0) return 0;
+  if (p.dtype != ODA_BF16 || a.rows.source != kSrcRing || (p.G != 1 && p.G != 2)) return (int)hipErrorInvalidValue;
+  dim3 grid(a.splits, a.Hkv, batch);
+  const dim3 block(kGroupThreads);
+  if (p.D == 128) {
+    if (p.G == 1) hipLaunchKernelGGL((merge_wait_test_kernel<ODA_BF16, 128, 1>), grid, block, 0, s, a, withheld, spin_limit);
+    else hipLaunchKernelGGL((merge_wait_test_kernel<ODA_BF16, 128, 2>), grid, block, 0, s, a, withheld, spin_limit);
+  } else {
+    if (p.G == 1) hipLaunchKernelGGL((merge_wait_test_kernel<ODA_BF16, 64, 1>), grid, block, 0, s, a, withheld, spin_limit);
+    else hipLaunchKernelGGL((merge_wait_test_kernel<ODA_BF16, 64, 2>), grid, block, 0, s, a, withheld, spin_limit);
+  }
+  return (int)hipGetLastError();
 }
 
 int launch_gate(const Plan& p, const oda_kv& kv, int32_t batch, const float* score, float theta,

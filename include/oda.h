@@ -348,6 +348,22 @@ oda_status oda_step_recall(const oda_dims* dims, const oda_kv* kv, int32_t batch
                            int64_t* counters, void* workspace, size_t workspace_bytes,
                            void* head_workspace, size_t head_workspace_bytes, oda_stream stream);
 
+/* Test support: the failure path of the Local pass's merge.  Runs
+ * oda_decode_local's pass (same arguments) with split `withheld_split` of
+ * every (request, KV head) leaving without storing its partial, and the
+ * merging workgroup giving up after `spin_limit` re-reads of the partial slots
+ * instead of about a second's worth.  Every workgroup exits normally; the
+ * merging ones find the withheld partial missing, set ODA_DEVERR_MERGE_WAIT
+ * in the workspace error word and write no output.  The workspace must then
+ * be prepared again (oda_workspace_init).  Built for bf16 K/V with GQA
+ * groups of 1 and 2; ODA_ERR_UNSUPPORTED for other shapes, when the pass
+ * would merge by ticket (more workgroups than compute units) or when
+ * withheld_split is not below the last split.  Not for production use. */
+oda_status oda_test_merge_wait(const oda_dims* dims, const oda_kv* kv, int32_t layer, int32_t batch,
+                               const void* q, const void* k_cur, const void* v_cur, float* out,
+                               float* lse, int32_t withheld_split, int32_t spin_limit,
+                               void* workspace, size_t workspace_bytes, oda_stream stream);
+
 /* Host.  Human-readable status name. */
 const char* oda_status_string(oda_status status);
 

@@ -438,6 +438,45 @@ FP8 = [
 ]
 
 
+def test_polling_merge_gives_up_and_flags_when_a_partial_never_arrives():
+    """The merging workgroup of a polling pass waits a bounded time for the
+    other splits' partials.  oda_test_merge_wait runs a Local pass in which
+    split 0 of every (request, KV head) stores no partial, and caps the wait at
+    a few re-reads: the call returns, every workgroup exits, the workspace's
+    error word carries ODA_DEVERR_MERGE_WAIT and no output or lse is written.
+    Once the workspace is prepared again, the same pass matches the oracle with
+    a clean error word."""
+    wl = _small("merge_wait", prefill=(300, 1200, 2600), steps=1, seed=191)
+    st = DecodeState(wl, gen_device="cpu")
+    st.prefill()
+    q = W.gen_queries(wl, "cpu")[0].cuda()
+    k_new, v_new = st.decode_inputs()
+    score = np.full((1, wl.batch), -1.0, np.float32)  # nothing fires: the outputs are the Local pass's
+    ks, vs = oracle_sequences(st)
+    want = orc.decode_run(oracle_cfg(wl), wl.prefill, ks, vs, words(q.unsqueeze(0)), score)
+    layer = 1
+    args = (q[layer].contiguous(), k_new[0, layer].contiguous(), v_new[0, layer].contiguous())
+    shape = (wl.batch, wl.num_q_heads, wl.head_dim)
+    out = torch.full(shape, 7.0, device="cuda")
+    lse = torch.full(shape[:2], 7.0, device="cuda")
+    with pytest.raises(B.OdaError):  # the last split merges; it cannot be the withheld one
+        B.test_merge_wait(st.dims, st.kv, layer, wl.batch, *args, out, lse, 10_000, 4, st.workspace)
+    B.test_merge_wait(st.dims, st.kv, layer, wl.batch, *args, out, lse, 0, 4, st.workspace)
+    torch.cuda.synchronize()
+    err = st.device_error()
+    say(f"withheld partial: error word {err}")
+    assert err == B.DEVERR_MERGE_WAIT
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all()), "a merge that gave up writes nothing"
+    B.workspace_init(st.dims, wl.batch, st.workspace)
+    B.decode_local(st.dims, st.kv, layer, wl.batch, *args, out, lse, st.workspace)
+    torch.cuda.synchronize()
+    assert st.device_error() == 0
+    assert_outputs_close(out.cpu().numpy()[None, None], want["out"][:, layer:layer + 1], wl.dtype,
+                         "after the workspace is prepared again")
+    lse_err = float(np.abs(lse.cpu().numpy() - want["lse"][0, layer]).max())
+    assert lse_err <= LSE_TOL[wl.dtype], lse_err
+
+
 @pytest.mark.parametrize("wl", FP8, ids=[w.name for w in FP8])
 def test_fp8_kv_runs_match_oracle(wl):
     """E4M3 codes in the caches, rings and new-token inputs, bf16 queries,
