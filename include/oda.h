@@ -354,7 +354,9 @@ oda_status oda_step_recall(const oda_dims* dims, const oda_kv* kv, int32_t batch
  * merging workgroup giving up after `spin_limit` re-reads of the partial slots
  * instead of about a second's worth.  Every workgroup exits normally; the
  * merging ones find the withheld partial missing, set ODA_DEVERR_MERGE_WAIT
- * in the workspace error word and write no output.  The workspace must then
+ * in the workspace error word and write no output (a request whose Local set
+ * spans fewer than withheld_split + 2 splits merges normally: the withheld
+ * split is then its merging split or has no rows).  The workspace must then
  * be prepared again (oda_workspace_init).  Built for bf16 K/V with GQA
  * groups of 1 and 2; ODA_ERR_UNSUPPORTED for other shapes, when the pass
  * would merge by ticket (more workgroups than compute units) or when
